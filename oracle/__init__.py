@@ -1,0 +1,257 @@
+"""CPU oracle for the MoE dispatch-preprocessing path (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: this package is the slow, plain reference the GPU
+library is checked against.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import it; the product package
+never does, and it is never a fallback for the GPU path.
+
+The arithmetic lives in ``mxq_oracle.c`` (plain C, built with
+``-O2 -ffp-contract=off -fopenmp``); see that file's header for the pages each
+function follows and the readings taken where they are silent.  This module
+only converts numpy arrays to pointers.
+
+Arrays: bf16 data is carried as ``uint16`` (the upper half of a binary32
+word), fp8 e4m3fn and scale bytes as ``uint8``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_u32 = ctypes.c_uint32
+_p = ctypes.c_void_p
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (it is C, not part of the GPU library)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+             "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        sig = {
+            "ora_e4m3_decode": (ctypes.c_double, [ctypes.c_uint8]),
+            "ora_e4m3_encode": (ctypes.c_uint8, [ctypes.c_double]),
+            "ora_bf16_round": (ctypes.c_uint16, [ctypes.c_float]),
+            "ora_bf16_round_array": (None, [_p, _i64, _p]),
+            "ora_e4m3_encode_array_f32": (None, [_p, _i64, _p]),
+            "ora_e4m3_decode_array": (None, [_p, _i64, _p]),
+            "ora_e4m3_encode_bits_range": (None, [_u32, _i64, _p]),
+            "ora_pow2_scale_exponent": (_i32, [ctypes.c_double]),
+            "ora_quant_row": (None, [_p, _i32, _i32, _p, _p]),
+            "ora_compact_row_bound": (_i64, [_i64, _i32, _i32]),
+            "ora_should_use_masked": (_i32, [_i32, _i32]),
+            "ora_moe_layout": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _i64, _p, _p, _p, _p, _p, _p]),
+            "ora_scatter_quant": (None, [_p, _i64, _i64, _i32, _p, _i32, _i32,
+                                         _p, _i64, _p, _i64]),
+            "ora_mx_quant_live_rows": (None, [_p, _i64, _i32, _i64, _p, _i32,
+                                              _i32, _p, _i64, _p, _i64]),
+            "ora_requant_per_token_to_per_tensor": (
+                None, [_p, _i64, _p, _i64, _i32, _p, _i64, _p]),
+            "ora_combine_f32": (None, [_p, _i64, _p, _p, _i64, _i32, _i32, _p,
+                                       _i64]),
+            "ora_combine_f64": (None, [_p, _i64, _p, _p, _i64, _i32, _i32, _p,
+                                       _p, _i64]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data if a.size else 0
+
+
+def _c(a, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+# ------------------------------------------------------------------ formats
+
+def e4m3_decode(b) -> np.ndarray:
+    b = _c(b, np.uint8)
+    out = np.empty(b.shape, np.float64)
+    lib().ora_e4m3_decode_array(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """Encode float32 values to e4m3fn bytes (nearest-even, saturating)."""
+    y = _c(y, np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().ora_e4m3_encode_array_f32(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def e4m3_encode_bits_range(w0: int, n: int) -> np.ndarray:
+    out = np.empty(n, np.uint8)
+    lib().ora_e4m3_encode_bits_range(w0, n, _ptr(out))
+    return out
+
+
+def bf16_round(x) -> np.ndarray:
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().ora_bf16_round_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def pow2_scale_exponent(amax: float) -> int:
+    return int(lib().ora_pow2_scale_exponent(float(amax)))
+
+
+def quant_row(x_bf16, G: int):
+    x = _c(x_bf16, np.uint16)
+    H = x.shape[-1]
+    q = np.empty(H, np.uint8)
+    s = np.empty(H // G, np.uint8)
+    lib().ora_quant_row(_ptr(x), H, G, _ptr(q), _ptr(s))
+    return q, s
+
+
+# ------------------------------------------------------------------- layout
+
+def compact_row_bound(num_assignments: int, num_experts: int,
+                      block_e: int = 128) -> int:
+    return int(lib().ora_compact_row_bound(num_assignments, num_experts,
+                                           block_e))
+
+
+def should_use_masked(num_experts: int, num_local_experts: int) -> bool:
+    return bool(lib().ora_should_use_masked(num_experts, num_local_experts))
+
+
+def moe_layout(topk_ids, expert_begin: int, num_local_experts: int,
+               kind: str, block_e: int = 128, capacity: int = 0,
+               num_rows: int | None = None):
+    """Returns dict(counts, expert_offsets, m_indices, masked_m, src2dst,
+    overflow, num_rows)."""
+    ids = _c(topk_ids, np.int32)
+    T, K = ids.shape
+    E = num_local_experts
+    k = {"compact": 0, "masked": 1}[kind]
+    if num_rows is None:
+        num_rows = (compact_row_bound(T * K, E, block_e) if k == 0
+                    else E * capacity)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    m_idx = np.empty(num_rows, np.int32)
+    masked_m = np.empty(E, np.int32)
+    src2dst = np.empty((T, K), np.int32)
+    ovf = np.zeros(1, np.int32)
+    rc = lib().ora_moe_layout(_ptr(ids), T, K, expert_begin, E, k, block_e,
+                              capacity, num_rows, _ptr(counts),
+                              _ptr(offsets), _ptr(m_idx), _ptr(masked_m),
+                              _ptr(src2dst), _ptr(ovf))
+    if rc != 0:
+        raise ValueError("num_rows too small for this routing")
+    return dict(counts=counts, expert_offsets=offsets, m_indices=m_idx,
+                masked_m=masked_m, src2dst=src2dst, overflow=int(ovf[0]),
+                num_rows=num_rows)
+
+
+# ----------------------------------------------------------- quantization
+
+def scatter_quant(x_bf16, src2dst, G: int, num_rows: int, q=None, s=None):
+    """Quantize each token row once and copy it to its destination rows.
+    ``q``/``s`` may be given pre-filled (untouched rows keep their bytes)."""
+    x = _c(x_bf16, np.uint16)
+    d = _c(src2dst, np.int32)
+    T, H = x.shape
+    K = d.shape[1] if d.ndim == 2 else 0
+    if q is None:
+        q = np.zeros((num_rows, H), np.uint8)
+    if s is None:
+        s = np.zeros((num_rows, H // G), np.uint8)
+    assert q.flags.c_contiguous and s.flags.c_contiguous
+    lib().ora_scatter_quant(_ptr(x), H, T, H, _ptr(d), K, G, _ptr(q),
+                            q.shape[1], _ptr(s), s.shape[1])
+    return q, s
+
+
+def mx_quant_live_rows(x_bf16, num_segments: int, live_counts, G: int = 32,
+                       q=None, s=None):
+    x = _c(x_bf16, np.uint16)
+    rows, H = x.shape
+    rps = rows // num_segments if num_segments else 0
+    live = _c(live_counts, np.int32)
+    if q is None:
+        q = np.zeros((rows, H), np.uint8)
+    if s is None:
+        s = np.zeros((rows, H // G), np.uint8)
+    lib().ora_mx_quant_live_rows(_ptr(x), H, num_segments, rps, _ptr(live), H,
+                                 G, _ptr(q), q.shape[1], _ptr(s), s.shape[1])
+    return q, s
+
+
+def requant_per_token_to_per_tensor(q_in, token_scales):
+    q = _c(q_in, np.uint8)
+    sc = _c(token_scales, np.float32)
+    T, H = q.shape
+    out = np.empty_like(q)
+    S = np.zeros(1, np.float32)
+    lib().ora_requant_per_token_to_per_tensor(_ptr(q), H, _ptr(sc), T, H,
+                                              _ptr(out), H, _ptr(S))
+    return out, float(S[0])
+
+
+def combine_f32(y_bf16, src2dst, weights):
+    """fp32 accumulator of the weighted combine, shape [T, H]."""
+    y = _c(y_bf16, np.uint16)
+    d = _c(src2dst, np.int32)
+    w = _c(weights, np.float32)
+    T, K = d.shape
+    H = y.shape[1]
+    acc = np.empty((T, H), np.float32)
+    lib().ora_combine_f32(_ptr(y), H, _ptr(d), _ptr(w), T, K, H, _ptr(acc), H)
+    return acc
+
+
+def combine(y_bf16, src2dst, weights, out_dtype: str = "bf16"):
+    acc = combine_f32(y_bf16, src2dst, weights)
+    if out_dtype == "f32":
+        return acc
+    return bf16_round(acc)
+
+
+def combine_f64(y_bf16, src2dst, weights):
+    y = _c(y_bf16, np.uint16)
+    d = _c(src2dst, np.int32)
+    w = _c(weights, np.float32)
+    T, K = d.shape
+    H = y.shape[1]
+    out = np.empty((T, H), np.float64)
+    mag = np.empty((T, H), np.float64)
+    lib().ora_combine_f64(_ptr(y), H, _ptr(d), _ptr(w), T, K, H, _ptr(out),
+                          _ptr(mag), H)
+    return out, mag

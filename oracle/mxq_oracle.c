@@ -1,0 +1,434 @@
+/*
+ * CPU oracle for the MoE dispatch-preprocessing path (fp8 e4m3 activations
+ * with power-of-two group scales).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
+ * GPU library is checked against.  Only the test suite, the package smoke
+ * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
+ * header, table or constant generator with the HIP library, and it must never
+ * serve as a fallback for it.
+ *
+ * Sources (the pages are summaries of sglang pull requests):
+ *   [P1] sglang PR #33128 page (DeepGEMM standard MoE dispatch, compact layout,
+ *        UE8M0 requant)
+ *   [P2] sglang PR #14162 page (DeepEP low-latency dispatch in fp8, per-token
+ *        to per-tensor requant)
+ *   [P3] sglang PR #29525 page (DeepEPv2 ElasticBuffer backend, psum layouts,
+ *        masked-slab repack)
+ *   [P4] sglang PR #36119 page (MXFP8 MoRI dispatch on MI355X, send-side
+ *        group-32 e8m0 quant over live tokens)
+ * Format definitions not on the pages: OCP 8-bit floating point (OFP8) E4M3
+ * ("e4m3fn": bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN, largest
+ * finite 448) and the OCP Microscaling E8M0 scale (one byte, value 2^(b-127)).
+ *
+ * Readings of points the pages leave open (each is listed in the design notes):
+ *   R1  fp8 e4m3 is OCP e4m3fn; encoding rounds to nearest, ties to even, and
+ *       saturates to +-448 (never produces NaN from a finite input).
+ *   R2  the power-of-two scale exponent of a group is the smallest integer e
+ *       with amax <= 448 * 2^e (no clipping), clamped to [-127, 127]; an
+ *       all-zero group gets e = -127.  Same rule for group 128 and group 32.
+ *   R3  slots inside an expert's region follow ascending flat assignment index
+ *       t*K + j (deterministic, stable).
+ *   R4  rows past the last expert's padded region, up to the static bound, are
+ *       padding rows (m_indices = -1), like the per-expert padding rows.
+ *   R5  masked layout: an expert's assignments beyond the slab capacity get no
+ *       slot (src2dst = -1) and raise the overflow flag; masked_m is clipped.
+ *   R6  per-token -> per-tensor requant: amax over dequantized values
+ *       fl32(dec(q) * s_t); S = fl32(amax / 448) (S = 1 when amax = 0);
+ *       inv = fl32(1 / S); q' = enc(fl32(fl32(dec(q) * s_t) * inv)).
+ *   R7  combine: fp32 accumulator from +0, one fused multiply-add per
+ *       assignment in ascending j, non-local assignments skipped, result
+ *       rounded to bf16 (nearest, ties to even) or kept as fp32.
+ *
+ * Floating-point: built with -ffp-contract=off.  Quantization arithmetic is
+ * done in double, where every step is exact (power-of-two scaling of values
+ * with at most 24 significant bits); the requant (R6) and combine (R7) steps
+ * are fp32 by definition of the readings, and have fp64 companions for the
+ * error bounds.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORA_E4M3_MAX 448.0
+
+/* ---------------------------------------------------------------- formats */
+
+/* bf16 is the upper half of an IEEE binary32 word. */
+static double bf16_to_double(uint16_t h) {
+  uint32_t w = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+static float bf16_to_float(uint16_t h) {
+  uint32_t w = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return f;
+}
+
+/* Decode one e4m3fn byte (OFP8 E4M3: value = (-1)^s * 2^(E-7) * (1 + m/8)
+ * for E >= 1, (-1)^s * 2^-6 * (m/8) for E = 0; S.1111.111 is NaN). */
+double ora_e4m3_decode(uint8_t b) {
+  int s = b >> 7;
+  int ef = (b >> 3) & 0xF;
+  int m = b & 0x7;
+  double mag;
+  if (ef == 15 && m == 7) return s ? -NAN : NAN;
+  if (ef == 0)
+    mag = ldexp((double)m, -9);
+  else
+    mag = ldexp((double)(8 + m), ef - 10);
+  return s ? -mag : mag;
+}
+
+/* Encode a real number to e4m3fn (R1).  The grid spacing at |y| is 2^-9 in
+ * the subnormal range (|y| < 2^-6) and 2^(floor(log2|y|) - 3) above it.
+ * |y| / spacing is exact in double, so the nearest-even choice below is the
+ * textbook rule applied to the exact value. */
+uint8_t ora_e4m3_encode(double y) {
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  double a = fabs(y);
+  if (isnan(y)) return sign | 0x7F;
+  if (isinf(a)) return sign | 0x7E;
+  if (a == 0.0) return sign;
+
+  double spacing;
+  if (a < ldexp(1.0, -6)) {
+    spacing = ldexp(1.0, -9);
+  } else {
+    int E;
+    frexp(a, &E); /* a = f * 2^E with f in [0.5, 1): floor(log2 a) = E - 1 */
+    spacing = ldexp(1.0, (E - 1) - 3);
+  }
+  double n = a / spacing; /* exact: division by a power of two */
+  double lo = floor(n);
+  double frac = n - lo; /* exact */
+  double r;
+  if (frac > 0.5)
+    r = lo + 1.0;
+  else if (frac < 0.5)
+    r = lo;
+  else
+    r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;
+  double v = r * spacing;
+  if (v > ORA_E4M3_MAX) v = ORA_E4M3_MAX; /* satfinite */
+  if (v == 0.0) return sign;
+
+  if (v < ldexp(1.0, -6)) { /* subnormal: v = m * 2^-9, m in 1..7 */
+    int m = (int)(v / ldexp(1.0, -9));
+    return sign | (uint8_t)m;
+  }
+  int E;
+  frexp(v, &E);
+  int e = E - 1;                                 /* v = 2^e * (1 + m/8) */
+  int m = (int)(v / ldexp(1.0, e - 3)) - 8;      /* 0..7 */
+  return sign | (uint8_t)(((e + 7) << 3) | m);
+}
+
+/* Round a binary32 value to bf16, nearest with ties to even, by comparing the
+ * exact distances to the two neighbouring bf16 values. */
+uint16_t ora_bf16_round(float x) {
+  uint32_t w;
+  memcpy(&w, &x, sizeof w);
+  uint16_t sign = (uint16_t)((w >> 16) & 0x8000);
+  if (isnan(x)) return sign | 0x7FC0;
+  if (isinf(x)) return (uint16_t)(w >> 16);
+  uint32_t lo_bits = w & 0xFFFF0000u; /* truncation toward zero */
+  uint16_t lo_h = (uint16_t)(lo_bits >> 16);
+  double a = fabs((double)x);
+  double lo = fabs(bf16_to_double(lo_h));
+  if (a == lo) return lo_h;
+  /* spacing of bf16 at lo: exponent field of lo, 7 fraction bits */
+  int ef = (int)((lo_bits >> 23) & 0xFF);
+  double spacing = (ef == 0) ? ldexp(1.0, -133) : ldexp(1.0, ef - 127 - 7);
+  double hi = lo + spacing;
+  double dlo = a - lo, dhi = hi - a;
+  uint16_t mag_lo = lo_h & 0x7FFF;
+  uint16_t mag;
+  if (dlo < dhi)
+    mag = mag_lo;
+  else if (dhi < dlo)
+    mag = (uint16_t)(mag_lo + 1);
+  else
+    mag = (mag_lo & 1) ? (uint16_t)(mag_lo + 1) : mag_lo;
+  return sign | mag;
+}
+
+void ora_bf16_round_array(const float* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ora_bf16_round(x[i]);
+}
+
+void ora_e4m3_encode_array_f32(const float* y, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = ora_e4m3_encode((double)y[i]);
+}
+
+void ora_e4m3_decode_array(const uint8_t* b, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ora_e4m3_decode(b[i]);
+}
+
+/* Encode every binary32 bit pattern w in [w0, w0 + n) (used by the exhaustive
+ * codec check; the pattern itself is the input). */
+void ora_e4m3_encode_bits_range(uint32_t w0, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t w = w0 + (uint32_t)i;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    out[i] = ora_e4m3_encode((double)f);
+  }
+}
+
+/* --------------------------------------------------- power-of-two scales */
+
+/* R2: smallest integer e with amax <= 448 * 2^e, clamped to [-127, 127]
+ * [P1 Implementation breakdown item 3: quantize with a UE8M0 scale directly;
+ *  P4 Implementation breakdown item 1: group-32 e8m0 scales, one byte each]. */
+int ora_pow2_scale_exponent(double amax) {
+  if (!(amax > 0.0)) return -127;
+  int e = (int)ceil(log2(amax / ORA_E4M3_MAX));
+  while (ldexp(ORA_E4M3_MAX, e) < amax) ++e;
+  while (ldexp(ORA_E4M3_MAX, e - 1) >= amax) --e;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+/* One row of H bf16 values -> H e4m3 bytes and H/G scale bytes (byte = e+127).
+ * Each group's payload is x * 2^-e, which is exact in double. */
+void ora_quant_row(const uint16_t* x, int32_t H, int32_t G, uint8_t* q,
+                   uint8_t* s) {
+  for (int32_t g = 0; g < H / G; ++g) {
+    double amax = 0.0;
+    for (int32_t i = g * G; i < (g + 1) * G; ++i) {
+      double v = fabs(bf16_to_double(x[i]));
+      if (v > amax) amax = v;
+    }
+    int e = ora_pow2_scale_exponent(amax);
+    for (int32_t i = g * G; i < (g + 1) * G; ++i)
+      q[i] = ora_e4m3_encode(ldexp(bf16_to_double(x[i]), -e));
+    s[g] = (uint8_t)(e + 127);
+  }
+}
+
+/* ------------------------------------------------------------- layout */
+
+/* Static compact row bound [P1 Key source snippets, _get_compact_all_tokens]:
+ * every non-empty expert takes at least one block, the remaining assignments
+ * fill whole blocks: block_e * (n + (A - n) // block_e), n = min(A, E). */
+int64_t ora_compact_row_bound(int64_t num_assignments, int32_t num_experts,
+                              int32_t block_e) {
+  int64_t n = num_assignments < num_experts ? num_assignments : num_experts;
+  return (int64_t)block_e * (n + (num_assignments - n) / block_e);
+}
+
+/* Layout choice [P1 Key source snippets, _should_use_masked_standard_layout]:
+ * masked iff expert parallelism is on (global > local) and local <= 32. */
+int32_t ora_should_use_masked(int32_t num_experts, int32_t num_local_experts) {
+  return (num_experts > num_local_experts && num_local_experts <= 32) ? 1 : 0;
+}
+
+/* Routing -> expert-grouped layout.
+ *   kind 0 (compact) [P1 Implementation breakdown items 2-3; P1 Key source
+ *     snippets, _fwd_kernel_ep_scatter_1]: expert e owns rows
+ *     [offsets[e], offsets[e] + padded_e), padded_e = ceil(c_e/block_e)*block_e;
+ *     rows holding an assignment carry m_indices = e, the rest -1 (R4).
+ *   kind 1 (masked slab) [P3 Implementation breakdown item 2, Key source
+ *     snippets: masked slab [E, max_m, hidden] with masked_m]: expert e owns
+ *     rows [e*cap, (e+1)*cap); slots >= cap are dropped and flagged (R5).
+ * Slots follow R3.  Returns 0, or 1 if num_rows is too small for the layout
+ * (nothing is written then). */
+int32_t ora_moe_layout(const int32_t* topk_ids, int64_t T, int32_t K,
+                       int32_t expert_begin, int32_t E, int32_t kind,
+                       int32_t block_e, int32_t cap, int64_t num_rows,
+                       int32_t* counts, int32_t* offsets, int32_t* m_indices,
+                       int32_t* masked_m, int32_t* src2dst,
+                       int32_t* overflow) {
+  int64_t A = T * (int64_t)K;
+  int32_t* fill = (int32_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
+  int32_t* cnt = (int32_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
+  int64_t* off = (int64_t*)calloc((size_t)E + 1, sizeof(int64_t));
+
+  /* a1: histogram of local assignments */
+  for (int64_t i = 0; i < A; ++i) {
+    int64_t e = (int64_t)topk_ids[i] - expert_begin;
+    if (e >= 0 && e < E) cnt[e] += 1;
+  }
+  /* a2: region starts */
+  off[0] = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    int64_t region;
+    if (kind == 0)
+      region = ((int64_t)cnt[e] + block_e - 1) / block_e * block_e;
+    else
+      region = cap;
+    off[e + 1] = off[e] + region;
+  }
+  if (off[E] > num_rows) {
+    free(fill); free(cnt); free(off);
+    return 1;
+  }
+  /* a3: stable slots in ascending flat index */
+  int32_t ovf = 0;
+  for (int64_t i = 0; i < A; ++i) {
+    int64_t e = (int64_t)topk_ids[i] - expert_begin;
+    if (e < 0 || e >= E) {
+      src2dst[i] = -1;
+      continue;
+    }
+    int32_t r = fill[e]++;
+    if (kind == 1 && r >= cap) {
+      src2dst[i] = -1;
+      ovf = 1;
+    } else {
+      src2dst[i] = (int32_t)(off[e] + r);
+    }
+  }
+  for (int32_t e = 0; e < E; ++e) {
+    counts[e] = cnt[e];
+    offsets[e] = (int32_t)off[e];
+    if (masked_m) masked_m[e] = (kind == 1 && cnt[e] > cap) ? cap : cnt[e];
+  }
+  offsets[E] = (int32_t)off[E];
+  if (m_indices) {
+    for (int64_t r = 0; r < num_rows; ++r) m_indices[r] = -1;
+    for (int32_t e = 0; e < E; ++e) {
+      int32_t live = (kind == 1 && cnt[e] > cap) ? cap : cnt[e];
+      for (int32_t r = 0; r < live; ++r) m_indices[off[e] + r] = e;
+    }
+  }
+  *overflow = ovf;
+  free(fill); free(cnt); free(off);
+  return 0;
+}
+
+/* ---------------------------------------------------- scatter + quant */
+
+/* Every token row is quantized once and its bytes are copied to each of its
+ * destination rows [P1 Implementation breakdown item 3: fused quant+scatter
+ * with UE8M0 scales].  Rows that are no destination are not touched. */
+void ora_scatter_quant(const uint16_t* x, int64_t ld_x, int64_t T, int32_t H,
+                       const int32_t* src2dst, int32_t K, int32_t G,
+                       uint8_t* q, int64_t ld_q, uint8_t* s, int64_t ld_s) {
+#pragma omp parallel
+  {
+    uint8_t* rq = (uint8_t*)malloc((size_t)H);
+    uint8_t* rs = (uint8_t*)malloc((size_t)(H / G));
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      int any = 0;
+      for (int32_t j = 0; j < K; ++j) any |= src2dst[t * K + j] >= 0;
+      if (!any) continue;
+      ora_quant_row(x + t * ld_x, H, G, rq, rs);
+      for (int32_t j = 0; j < K; ++j) {
+        int64_t d = src2dst[t * K + j];
+        if (d < 0) continue;
+        memcpy(q + d * ld_q, rq, (size_t)H);
+        memcpy(s + d * ld_s, rs, (size_t)(H / G));
+      }
+    }
+    free(rq);
+    free(rs);
+  }
+}
+
+/* Send-side quant over live rows only [P4 Features & motivation;
+ * Implementation breakdown item 1]: segment g holds rows
+ * [g*rows_per_segment, (g+1)*rows_per_segment); its first live[g] rows are
+ * quantized, the others are not touched. */
+void ora_mx_quant_live_rows(const uint16_t* x, int64_t ld_x,
+                            int32_t num_segments, int64_t rows_per_segment,
+                            const int32_t* live, int32_t H, int32_t G,
+                            uint8_t* q, int64_t ld_q, uint8_t* s,
+                            int64_t ld_s) {
+  for (int32_t g = 0; g < num_segments; ++g) {
+    int64_t n = live[g];
+    if (n > rows_per_segment) n = rows_per_segment;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      int64_t row = (int64_t)g * rows_per_segment + r;
+      ora_quant_row(x + row * ld_x, H, G, q + row * ld_q, s + row * ld_s);
+    }
+  }
+}
+
+/* ------------------------------------------------------------- requant */
+
+/* Per-token scaled fp8 -> one per-tensor scale [P2 Implementation breakdown
+ * items 1-2], reading R6.  Input scales are per token, fp32, positive. */
+void ora_requant_per_token_to_per_tensor(const uint8_t* q_in, int64_t ld_in,
+                                         const float* token_scales, int64_t T,
+                                         int32_t H, uint8_t* q_out,
+                                         int64_t ld_out, float* tensor_scale) {
+  float amax = 0.0f;
+  for (int64_t t = 0; t < T; ++t) {
+    double row = 0.0;
+    for (int32_t j = 0; j < H; ++j) {
+      double v = fabs(ora_e4m3_decode(q_in[t * ld_in + j]));
+      if (v > row) row = v;
+    }
+    float rq = (float)row * token_scales[t];
+    if (rq > amax) amax = rq;
+  }
+  float S = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+  float inv = 1.0f / S;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t j = 0; j < H; ++j) {
+      float v = (float)ora_e4m3_decode(q_in[t * ld_in + j]);
+      float deq = v * token_scales[t];
+      float y = deq * inv;
+      q_out[t * ld_out + j] = ora_e4m3_encode((double)y);
+    }
+  }
+  *tensor_scale = S;
+}
+
+/* ------------------------------------------------------------- combine */
+
+/* Un-permute with top-k weights [P1 Implementation breakdown item 2 and
+ * Risks item 2 (post-permute through src2dst); P3 Implementation breakdown
+ * item 3 (top-k weights applied on real rows only)], reading R7.
+ * acc_out receives the fp32 accumulator per element. */
+void ora_combine_f32(const uint16_t* y, int64_t ld_y, const int32_t* src2dst,
+                     const float* w, int64_t T, int32_t K, int32_t H,
+                     float* acc_out, int64_t ld_out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t h = 0; h < H; ++h) {
+      float acc = 0.0f;
+      for (int32_t j = 0; j < K; ++j) {
+        int64_t d = src2dst[t * K + j];
+        if (d < 0) continue;
+        acc = fmaf(w[t * K + j], bf16_to_float(y[d * ld_y + h]), acc);
+      }
+      acc_out[t * ld_out + h] = acc;
+    }
+  }
+}
+
+/* The same sum in double (exact products, one rounding per addition); the
+ * reference for the error bound of the fp32 combine. */
+void ora_combine_f64(const uint16_t* y, int64_t ld_y, const int32_t* src2dst,
+                     const float* w, int64_t T, int32_t K, int32_t H,
+                     double* out, double* abs_sum, int64_t ld_out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t h = 0; h < H; ++h) {
+      double acc = 0.0, mag = 0.0;
+      for (int32_t j = 0; j < K; ++j) {
+        int64_t d = src2dst[t * K + j];
+        if (d < 0) continue;
+        double p = (double)w[t * K + j] * bf16_to_double(y[d * ld_y + h]);
+        acc += p;
+        mag += fabs(p);
+      }
+      out[t * ld_out + h] = acc;
+      abs_sum[t * ld_out + h] = mag;
+    }
+  }
+}

@@ -1,0 +1,223 @@
+"""Pins for the oracle's data-moving steps: scatter+quant, live-row MX quant,
+per-token -> per-tensor requant and the weighted combine."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic_inputs as si
+
+CANARY = 0xA5
+
+
+def dec(b):
+    return torch.from_numpy(np.ascontiguousarray(b, np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def bf16_vals(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(
+        np.float64)
+
+
+def check_rows_bound(x_bits, q, s, G):
+    x = bf16_vals(x_bits)
+    e = np.repeat(s.astype(np.int64) - 127, G, axis=-1)
+    deq = dec(q) * np.exp2(e.astype(np.float64))
+    tol = np.maximum(np.abs(x) * 2.0 ** -4, np.exp2((e - 10).astype(float)))
+    assert (np.abs(deq - x) <= tol).all()
+
+
+# --------------------------------------------------------- scatter + quant
+
+@pytest.mark.parametrize("G,H", [(128, 256), (32, 96), (128, 640), (32, 7168)])
+def test_scatter_quant_copies_and_canary(ora, G, H):
+    rng = np.random.default_rng(G + H)
+    T, E, K = 37, 6, 3
+    x = si.gaussian_bf16(rng, (T, H))
+    ids = si.uniform_topk(rng, T, 9, K)   # experts 6..8 are not local
+    lay = ora.moe_layout(ids, 0, E, "compact", block_e=16)
+    R = lay["num_rows"]
+    q = np.full((R, H), CANARY, np.uint8)
+    s = np.full((R, H // G), CANARY, np.uint8)
+    ora.scatter_quant(x, lay["src2dst"], G, R, q, s)
+    m = lay["m_indices"]
+    assert (q[m < 0] == CANARY).all() and (s[m < 0] == CANARY).all()
+    for t in range(T):
+        rq, rs = ora.quant_row(x[t], G)
+        for d in lay["src2dst"][t]:
+            if d >= 0:
+                assert np.array_equal(q[d], rq) and np.array_equal(s[d], rs)
+    live = m >= 0
+    src_tok = np.empty(R, np.int64)
+    for t in range(T):
+        for d in lay["src2dst"][t]:
+            if d >= 0:
+                src_tok[d] = t
+    check_rows_bound(x[src_tok[live]], q[live], s[live], G)
+
+
+def test_scatter_quant_row_column_fixture(ora):
+    """Each token row holds its own value, doubled on odd columns: a row mix-up
+    or a column shift in the scatter lands on a different dequantized value."""
+    T, H, G = 50, 640, 128
+    base = (np.arange(T) % 200 + 1).astype(np.float32)[:, None]
+    gain = 1.0 + (np.arange(H) % 2).astype(np.float32)[None, :]
+    x = si.to_bf16_bits(base * gain)
+    ids = (np.arange(T * 2).reshape(T, 2) % 5).astype(np.int32)
+    lay = ora.moe_layout(ids, 0, 5, "compact", block_e=8)
+    q, s = ora.scatter_quant(x, lay["src2dst"], G, lay["num_rows"])
+    for t in range(T):
+        for d in lay["src2dst"][t]:
+            e = np.repeat(s[d].astype(np.int64) - 127, G)
+            v = dec(q[d]) * np.exp2(e.astype(float))
+            want = bf16_vals(x[t])
+            assert np.allclose(v, want, rtol=2.0 ** -4)
+            assert np.all(v[1::2] > v[0::2])
+
+
+def test_masked_scatter_matches_compact_bytes(ora):
+    """Both layouts hold byte-identical rows for each assignment."""
+    b = si.decode_masked(H=512)
+    comp = ora.moe_layout(b.topk_ids, 0, 32, "compact")
+    mask = ora.moe_layout(b.topk_ids, 0, 32, "masked", capacity=128)
+    qc, sc = ora.scatter_quant(b.x, comp["src2dst"], 128, comp["num_rows"])
+    qm, sm = ora.scatter_quant(b.x, mask["src2dst"], 128, mask["num_rows"])
+    dc, dm = comp["src2dst"], mask["src2dst"]
+    assert np.array_equal(dc >= 0, dm >= 0)
+    sel = dc >= 0
+    assert np.array_equal(qc[dc[sel]], qm[dm[sel]])
+    assert np.array_equal(sc[dc[sel]], sm[dm[sel]])
+
+
+# ----------------------------------------------------------- live rows (MX)
+
+def test_live_rows_only_live_written(ora):
+    lr = si.live_rows(num_segments=4, rows_per_segment=24, H=256,
+                      live_counts=[3, 0, 24, 7])
+    rows, H = lr.x.shape
+    q = np.full((rows, H), CANARY, np.uint8)
+    s = np.full((rows, H // 32), CANARY, np.uint8)
+    ora.mx_quant_live_rows(lr.x, 4, lr.live_counts, 32, q, s)
+    for g in range(4):
+        for r in range(24):
+            row = g * 24 + r
+            if r < lr.live_counts[g]:
+                rq, rs = ora.quant_row(lr.x[row], 32)
+                assert np.array_equal(q[row], rq) and np.array_equal(s[row], rs)
+            else:
+                assert (q[row] == CANARY).all() and (s[row] == CANARY).all()
+
+
+def test_live_rows_counts_above_segment_are_clipped(ora):
+    lr = si.live_rows(num_segments=2, rows_per_segment=4, H=64,
+                      live_counts=[9, 1])
+    q = np.full((8, 64), CANARY, np.uint8)
+    s = np.full((8, 2), CANARY, np.uint8)
+    ora.mx_quant_live_rows(lr.x, 2, lr.live_counts, 32, q, s)
+    assert (q[0:4] != CANARY).any(axis=1).all()
+    assert (q[5:8] == CANARY).all()
+
+
+# ---------------------------------------------------------------- requant
+
+def test_requant_identity_for_equal_power_of_two_scales(ora):
+    """Every token scale 2^k and every row's largest magnitude 448: the
+    per-tensor scale is 2^k and every byte is unchanged."""
+    rng = np.random.default_rng(1)
+    q, _ = si.per_token_fp8(rng, 64, 256)
+    for k in (-8, 0, 3):
+        s = np.full(64, 2.0 ** k, np.float32)
+        out, S = ora.requant_per_token_to_per_tensor(q, s)
+        assert S == 2.0 ** k
+        assert np.array_equal(out, q)
+
+
+def test_requant_properties(ora):
+    rb = si.requant_input(T=300, H=512)
+    out, S = ora.requant_per_token_to_per_tensor(rb.q, rb.scales)
+    x = dec(rb.q) * rb.scales[:, None].astype(np.float64)
+    t, j = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert out[t, j] & 0x7F == 0x7E                   # argmax -> 448
+    assert np.float32(np.abs(x).max() / 448.0) == np.float32(S)
+    assert ((out & 0x7F) <= 0x7E).all()               # no NaN, |q'| <= 448
+    y = dec(out) * S
+    tol = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * S) + \
+        np.abs(x) * 2.0 ** -22
+    assert (np.abs(y - x) <= tol).all()
+
+
+def test_requant_zero_input(ora):
+    q = np.zeros((4, 64), np.uint8)
+    q[1] = 0x80
+    out, S = ora.requant_per_token_to_per_tensor(q, np.ones(4, np.float32))
+    assert S == 1.0 and np.array_equal(out, q)
+
+
+# ---------------------------------------------------------------- combine
+
+def place_expert_outputs(yv_per_assign, src2dst, num_rows, H):
+    """Put the per-assignment expert outputs at their layout rows; every other
+    row is NaN (padding is never read)."""
+    y = np.full((num_rows, H), 0x7FC0, np.uint16)
+    sel = src2dst >= 0
+    y[src2dst[sel]] = yv_per_assign[sel]
+    return y
+
+
+def test_masked_and_compact_combine_identically(ora):
+    """Same routing, same per-assignment expert outputs, two layouts: the
+    combined tokens are bit-identical (the masked-vs-compact end-to-end
+    equivalence the standard-dispatch tests check)."""
+    b = si.decode_masked(H=384)
+    rng = np.random.default_rng(9)
+    ya = si.gaussian_bf16(rng, (b.T, b.K, b.H))
+    comp = ora.moe_layout(b.topk_ids, 0, 32, "compact")
+    mask = ora.moe_layout(b.topk_ids, 0, 32, "masked", capacity=128)
+    yc = place_expert_outputs(ya, comp["src2dst"], comp["num_rows"], b.H)
+    ym = place_expert_outputs(ya, mask["src2dst"], mask["num_rows"], b.H)
+    oc = ora.combine(yc, comp["src2dst"], b.topk_weights)
+    om = ora.combine(ym, mask["src2dst"], b.topk_weights)
+    assert np.array_equal(oc, om)
+    assert np.isfinite(bf16_vals(oc)).all()
+
+
+def test_combine_one_hot_and_empty_tokens(ora):
+    rng = np.random.default_rng(2)
+    T, H, E = 20, 128, 4
+    ids = si.uniform_topk(rng, T, 8, 2)
+    lay = ora.moe_layout(ids, 0, E, "compact", block_e=4)
+    y = si.gaussian_bf16(rng, (lay["num_rows"], H))
+    si.poison_padding_rows(y, lay["m_indices"])
+    w = np.zeros((T, 2), np.float32)
+    w[:, 0] = 1.0
+    out = ora.combine(y, lay["src2dst"], w)
+    for t in range(T):
+        d0 = lay["src2dst"][t, 0]
+        if d0 >= 0:
+            assert np.array_equal(out[t], y[d0])
+        elif lay["src2dst"][t, 1] < 0:
+            assert (out[t] == 0).all()                # +0 rows
+    assert np.isfinite(bf16_vals(out)).all()
+
+
+def test_combine_vs_float64(ora):
+    b = si.tiny()
+    lay = ora.moe_layout(b.topk_ids, 0, 8, "compact")
+    rng = np.random.default_rng(4)
+    y = si.gaussian_bf16(rng, (lay["num_rows"], b.H))
+    si.poison_padding_rows(y, lay["m_indices"])
+    acc = ora.combine_f32(y, lay["src2dst"], b.topk_weights)
+    ref, mag = ora.combine_f64(y, lay["src2dst"], b.topk_weights)
+    assert (np.abs(acc - ref) <= 1e-6 * mag + 1e-30).all()
+    out = bf16_vals(ora.combine(y, lay["src2dst"], b.topk_weights))
+    assert (np.abs(out - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * mag).all()
+    # the plain float64 numpy sum agrees as well
+    w = b.topk_weights.astype(np.float64)
+    yv = bf16_vals(y)
+    manual = np.zeros((b.T, b.H))
+    for t in range(b.T):
+        for j in range(b.K):
+            d = lay["src2dst"][t, j]
+            if d >= 0:
+                manual[t] += w[t, j] * yv[d]
+    assert np.allclose(manual, ref, rtol=1e-12, atol=1e-12)
