@@ -1,0 +1,379 @@
+"""MoE expert-dispatch preprocessing with fp8 e4m3 activations and
+power-of-two group scales, on MI355X (gfx950).
+
+Thin Python binding over ``libmxq.so`` (declared in ``include/mxq.h``).  The
+functions carry the C names; they check tensor dtypes, shapes and devices,
+allocate missing outputs with ``torch.empty`` and pass raw pointers plus the
+current HIP stream.  Every step of the path runs in the library's HIP
+kernels; there is no CPU or PyTorch fallback: without the built library every
+call raises.
+
+Byte formats: fp8 payloads are ``torch.uint8`` tensors holding OCP e4m3fn
+bytes (``.view(torch.float8_e4m3fn)`` reinterprets them); a scale byte b
+means 2^(b - 127) (``.view(torch.float8_e8m0fnu)``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MxqError", "lib", "SCALE_FORMATS",
+    "moe_compact_row_bound", "moe_should_use_masked",
+    "moe_layout_workspace_bytes", "requant_workspace_bytes",
+    "moe_layout", "moe_read_overflow", "moe_scatter_quant",
+    "mx_quant_live_rows", "live_rows_view",
+    "requant_per_token_to_per_tensor", "moe_combine", "mxq_e4m3_encode_f32",
+    "mxq_abi_version",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxq.so")
+
+MXQ_OK = 0
+MXQ_ERR_CAPACITY_OVERFLOW = 3
+LAYOUT_KINDS = {"compact": 0, "masked": 1}
+SCALE_FORMATS = {"ue8m0_g128": (0, 128), "e8m0_g32": (1, 32)}
+OUT_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+
+_i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, \
+    ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_compact_row_bound": (_i64, [_i64, _i32, _i32]),
+    "moe_should_use_masked": (_i32, [_i32, _i32]),
+    "moe_layout_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "requant_workspace_bytes": (_sz, [_i64, _i32]),
+    "moe_layout": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                          _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_read_overflow": (_i32, [_p, _p, _p]),
+    "moe_scatter_quant": (_i32, [_p, _i64, _i64, _i32, _p, _i32, _i32, _p,
+                                 _i64, _p, _i64, _i64, _p]),
+    "mx_quant_live_rows": (_i32, [_p, _i64, _i32, _i64, _p, _i32, _i32, _p,
+                                  _i64, _p, _i64, _p]),
+    "requant_per_token_to_per_tensor": (_i32, [_p, _i64, _p, _i64, _i32, _p,
+                                               _i64, _p, _p, _sz, _p]),
+    "moe_combine": (_i32, [_p, _i64, _i64, _p, _p, _i64, _i32, _i32, _p, _i64,
+                           _i32, _p]),
+    "mxq_e4m3_encode_f32": (_i32, [_p, _i64, _p, _p]),
+    "mxq_status_string": (ctypes.c_char_p, [_i32]),
+    "mxq_abi_version": (_i32, []),
+}
+
+_lib = None
+
+
+class MxqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().mxq_status_string(status).decode()
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, status))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmxq.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libmxq.so is not built (expected at %s); build it with "
+                "`python -m fp8_mx_activation_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MXQ_OK:
+        raise MxqError(fn, status)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None or t.numel() == 0:
+        return None
+    return t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+
+
+def _rows(t: torch.Tensor, name: str, dtypes) -> int:
+    """Row stride (elements) of a 2-D tensor with unit column stride."""
+    if t.dtype not in dtypes:
+        raise TypeError("%s: dtype %s not in %s" % (name, t.dtype, dtypes))
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have unit column stride" % name)
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+_SCALE = (torch.uint8,) + ((torch.float8_e8m0fnu,)
+                           if hasattr(torch, "float8_e8m0fnu") else ())
+
+
+def _u8(t: torch.Tensor) -> torch.Tensor:
+    return t if t.dtype == torch.uint8 else t.view(torch.uint8)
+
+
+# ---------------------------------------------------------------- host-only
+
+def moe_compact_row_bound(num_assignments: int, num_local_experts: int,
+                          block_e: int = 128) -> int:
+    r = lib().moe_compact_row_bound(num_assignments, num_local_experts,
+                                    block_e)
+    if r < 0:
+        raise ValueError("invalid arguments to moe_compact_row_bound")
+    return int(r)
+
+
+def moe_should_use_masked(num_experts: int, num_local_experts: int) -> bool:
+    return bool(lib().moe_should_use_masked(num_experts, num_local_experts))
+
+
+def moe_layout_workspace_bytes(T: int, K: int, E: int) -> int:
+    return int(lib().moe_layout_workspace_bytes(T, K, E))
+
+
+def requant_workspace_bytes(T: int, H: int) -> int:
+    return int(lib().requant_workspace_bytes(T, H))
+
+
+def mxq_abi_version() -> int:
+    return int(lib().mxq_abi_version())
+
+
+# ------------------------------------------------------------------- layout
+
+def moe_layout(topk_ids: torch.Tensor, expert_begin: int,
+               num_local_experts: int, kind: str = "compact",
+               block_e: int = 128, capacity: int = 0,
+               num_rows: int | None = None, m_indices: bool = True,
+               out: dict | None = None,
+               workspace: torch.Tensor | None = None) -> dict:
+    """Expert-grouped layout of a top-k routing (see ``moe_layout`` in
+    mxq.h).  Returns a dict with ``counts``, ``expert_offsets``,
+    ``m_indices`` (or None), ``masked_m``, ``src2dst``, ``overflow_flag``
+    (device tensors) and ``num_rows``.  ``out`` may hold preallocated tensors
+    under the same keys."""
+    _dev(topk_ids, "topk_ids")
+    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
+        raise TypeError("topk_ids must be int32 [T, K]")
+    ids = topk_ids.contiguous()
+    T, K = ids.shape
+    E = num_local_experts
+    k = LAYOUT_KINDS[kind]
+    if num_rows is None:
+        num_rows = (moe_compact_row_bound(T * K, E, block_e) if k == 0
+                    else E * capacity)
+    dev = ids.device
+    o = dict(out or {})
+
+    def get(key, shape):
+        t = o.get(key)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.int32, device=dev)
+        elif t.dtype != torch.int32 or tuple(t.shape) != tuple(shape) or \
+                not t.is_contiguous():
+            raise ValueError("out[%r] must be contiguous int32 %s"
+                             % (key, shape))
+        return t
+
+    counts = get("counts", (E,))
+    offsets = get("expert_offsets", (E + 1,))
+    m_idx = get("m_indices", (num_rows,)) if m_indices else None
+    masked_m = get("masked_m", (E,))
+    src2dst = get("src2dst", (T, K))
+    flag = get("overflow_flag", (1,))
+    need = moe_layout_workspace_bytes(T, K, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().moe_layout(_ptr(ids), T, K, expert_begin, E, k, block_e,
+                          capacity, num_rows, _ptr(counts), _ptr(offsets),
+                          _ptr(m_idx), _ptr(masked_m), _ptr(src2dst),
+                          _ptr(flag), _ptr(workspace), workspace.numel(),
+                          _stream(ids))
+    _check("moe_layout", st)
+    return dict(counts=counts, expert_offsets=offsets, m_indices=m_idx,
+                masked_m=masked_m, src2dst=src2dst, overflow_flag=flag,
+                num_rows=num_rows)
+
+
+def moe_read_overflow(overflow_flag: torch.Tensor) -> int:
+    """Waits for the current stream and returns the flag (0 or 1)."""
+    _dev(overflow_flag, "overflow_flag")
+    v = ctypes.c_int32(0)
+    st = lib().moe_read_overflow(_ptr(overflow_flag), ctypes.addressof(v),
+                                 _stream(overflow_flag))
+    if st not in (MXQ_OK, MXQ_ERR_CAPACITY_OVERFLOW):
+        _check("moe_read_overflow", st)
+    return int(v.value)
+
+
+# ------------------------------------------------------------ quantization
+
+def moe_scatter_quant(x: torch.Tensor, src2dst: torch.Tensor, num_rows: int,
+                      fmt: str = "ue8m0_g128", q: torch.Tensor | None = None,
+                      scales: torch.Tensor | None = None):
+    """Quantize each bf16 token row once and write it to its destination
+    rows.  Returns ``(q [num_rows, H] uint8, scales [num_rows, H/G] uint8)``;
+    rows that are no destination keep the contents of a given ``q``/
+    ``scales`` (uninitialised if allocated here)."""
+    _dev(x, "x")
+    code, G = SCALE_FORMATS[fmt]
+    ld_x = _rows(x, "x", (torch.bfloat16,))
+    T, H = x.shape
+    if src2dst.dtype != torch.int32 or src2dst.dim() != 2 or \
+            src2dst.shape[0] != T or not src2dst.is_contiguous():
+        raise ValueError("src2dst must be contiguous int32 [T, K]")
+    K = src2dst.shape[1]
+    if q is None:
+        q = torch.empty((num_rows, H), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((num_rows, H // G), dtype=torch.uint8,
+                             device=x.device)
+    qq, ss = _u8(q), _u8(scales)
+    ld_q = _rows(qq, "q", (torch.uint8,))
+    ld_s = _rows(ss, "scales", (torch.uint8,))
+    if qq.shape[0] < num_rows or ss.shape[0] < num_rows:
+        raise ValueError("q/scales have fewer than num_rows rows")
+    st = lib().moe_scatter_quant(_ptr(x), ld_x, T, H, _ptr(src2dst), K, code,
+                                 _ptr(qq), ld_q, _ptr(ss), ld_s, num_rows,
+                                 _stream(x))
+    _check("moe_scatter_quant", st)
+    return q, scales
+
+
+def mx_quant_live_rows(x: torch.Tensor, num_segments: int,
+                       live_counts: torch.Tensor, fmt: str = "e8m0_g32",
+                       q: torch.Tensor | None = None,
+                       scales: torch.Tensor | None = None):
+    """Send-side quant of the live rows of a padded buffer of
+    ``num_segments`` equal segments (live rows at the head of each).
+    Returns the padded ``(q, scales)``; only live rows are written."""
+    _dev(x, "x")
+    _dev(live_counts, "live_counts")
+    code, G = SCALE_FORMATS[fmt]
+    ld_x = _rows(x, "x", (torch.bfloat16,))
+    rows, H = x.shape
+    if num_segments <= 0 or rows % num_segments:
+        raise ValueError("rows must split into num_segments equal segments")
+    if live_counts.dtype != torch.int32 or live_counts.numel() != \
+            num_segments or not live_counts.is_contiguous():
+        raise ValueError("live_counts must be contiguous int32 [segments]")
+    if q is None:
+        q = torch.empty((rows, H), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, H // G), dtype=torch.uint8,
+                             device=x.device)
+    qq, ss = _u8(q), _u8(scales)
+    ld_q = _rows(qq, "q", (torch.uint8,))
+    ld_s = _rows(ss, "scales", (torch.uint8,))
+    st = lib().mx_quant_live_rows(_ptr(x), ld_x, num_segments,
+                                  rows // num_segments, _ptr(live_counts), H,
+                                  code, _ptr(qq), ld_q, _ptr(ss), ld_s,
+                                  _stream(x))
+    _check("mx_quant_live_rows", st)
+    return q, scales
+
+
+def live_rows_view(q: torch.Tensor, scales: torch.Tensor, num_segments: int,
+                   live_counts_host):
+    """Host-side view of the live rows only: ``(q[n_live, H],
+    scales[n_live, H/G])``, which is ``(0, H/G)`` for an empty batch."""
+    rows = q.shape[0]
+    rps = rows // num_segments
+    sel = []
+    for g, n in enumerate(list(live_counts_host)):
+        n = max(0, min(int(n), rps))
+        sel.append((g * rps, g * rps + n))
+    if len(sel) == 1 or sum(b - a > 0 for a, b in sel) <= 1:
+        a, b = next(((a, b) for a, b in sel if b > a), (0, 0))
+        return q[a:b], scales[a:b]
+    return (torch.cat([q[a:b] for a, b in sel]),
+            torch.cat([scales[a:b] for a, b in sel]))
+
+
+def requant_per_token_to_per_tensor(q_in: torch.Tensor,
+                                    token_scales: torch.Tensor,
+                                    q_out: torch.Tensor | None = None,
+                                    tensor_scale: torch.Tensor | None = None,
+                                    workspace: torch.Tensor | None = None):
+    """fp8 rows with per-token fp32 scales -> fp8 rows with one fp32 scale.
+    Returns ``(q_out uint8 [T, H], tensor_scale float32 [1])``."""
+    _dev(q_in, "q_in")
+    qi = _u8(q_in)
+    ld_in = _rows(qi, "q_in", (torch.uint8,))
+    T, H = qi.shape
+    if token_scales.dtype != torch.float32 or token_scales.numel() != T or \
+            not token_scales.is_contiguous():
+        raise ValueError("token_scales must be contiguous float32 [T]")
+    if q_out is None:
+        q_out = torch.empty((T, H), dtype=torch.uint8, device=qi.device)
+    qo = _u8(q_out)
+    ld_out = _rows(qo, "q_out", (torch.uint8,))
+    if tensor_scale is None:
+        tensor_scale = torch.empty(1, dtype=torch.float32, device=qi.device)
+    need = requant_workspace_bytes(T, H)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qi.device)
+    st = lib().requant_per_token_to_per_tensor(
+        _ptr(qi), ld_in, _ptr(token_scales), T, H, _ptr(qo), ld_out,
+        tensor_scale.data_ptr(), _ptr(workspace), workspace.numel(),
+        _stream(qi))
+    _check("requant_per_token_to_per_tensor", st)
+    return q_out, tensor_scale
+
+
+def moe_combine(y: torch.Tensor, src2dst: torch.Tensor,
+                topk_weights: torch.Tensor,
+                out_dtype: torch.dtype = torch.bfloat16,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """Weighted un-permute of expert outputs ``y [num_rows, H]`` (bf16) back
+    to tokens: ``out [T, H]`` in bf16 or float32."""
+    _dev(y, "y")
+    ld_y = _rows(y, "y", (torch.bfloat16,))
+    num_rows, H = y.shape
+    if src2dst.dtype != torch.int32 or src2dst.dim() != 2 or \
+            not src2dst.is_contiguous():
+        raise ValueError("src2dst must be contiguous int32 [T, K]")
+    T, K = src2dst.shape
+    if topk_weights.dtype != torch.float32 or \
+            tuple(topk_weights.shape) != (T, K) or \
+            not topk_weights.is_contiguous():
+        raise ValueError("topk_weights must be contiguous float32 [T, K]")
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y.device)
+    code = OUT_DTYPES[out.dtype]
+    ld_out = _rows(out, "out", (out.dtype,))
+    st = lib().moe_combine(_ptr(y), ld_y, num_rows, _ptr(src2dst),
+                           _ptr(topk_weights), T, K, H, _ptr(out), ld_out,
+                           code, _stream(y))
+    _check("moe_combine", st)
+    return out
+
+
+def mxq_e4m3_encode_f32(x: torch.Tensor) -> torch.Tensor:
+    """The kernels' fp32 -> e4m3fn conversion, element by element."""
+    _dev(x, "x")
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    xc = x.contiguous()
+    out = torch.empty(xc.shape, dtype=torch.uint8, device=x.device)
+    st = lib().mxq_e4m3_encode_f32(_ptr(xc), xc.numel(), _ptr(out),
+                                   _stream(xc))
+    _check("mxq_e4m3_encode_f32", st)
+    return out

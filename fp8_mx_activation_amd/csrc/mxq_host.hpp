@@ -1,0 +1,75 @@
+// Host-side helpers shared by the entry points of libmxq: argument checks
+// and launch-error mapping.  Every check runs before any work is enqueued.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxq.h"
+
+namespace mxq {
+
+inline bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Launch status of the kernel just enqueued.
+inline mxq_status launch_status() {
+  return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+inline int group_of(mxq_scale_fmt fmt) {
+  switch (fmt) {
+    case MXQ_SCALE_UE8M0_G128:
+      return 128;
+    case MXQ_SCALE_E8M0_G32:
+      return 32;
+  }
+  return 0;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Threads per block for a row split in chunks of `per_lane` channels: a
+// whole number of 64-lane wavefronts, at most 1024.
+inline int row_block_threads(int64_t H, int per_lane) {
+  int64_t lanes = ceil_div(H, per_lane);
+  int64_t t = ceil_div(lanes, 64) * 64;
+  if (t < 64) t = 64;
+  if (t > 1024) t = 1024;
+  return (int)t;
+}
+
+}  // namespace mxq
+
+namespace mxq {
+
+// Layout work split: the T*K assignments are cut into at most kLayoutChunks
+// chunks of a whole number of 64-assignment steps; one wavefront owns a
+// chunk.  The split depends only on T*K, so the grid is static.
+constexpr int kLayoutChunks = 64;
+
+struct LayoutGeom {
+  int32_t nc;     // number of chunks (0 when there are no assignments)
+  int32_t chunk;  // assignments per chunk
+};
+
+inline LayoutGeom layout_geom(int64_t A) {
+  LayoutGeom g{0, 64};
+  if (A <= 0) return g;
+  int64_t nc = ceil_div(A, 64);
+  if (nc > kLayoutChunks) nc = kLayoutChunks;
+  int64_t chunk = ceil_div(ceil_div(A, nc), 64) * 64;
+  g.chunk = (int32_t)chunk;
+  g.nc = (int32_t)ceil_div(A, chunk);
+  return g;
+}
+
+inline size_t layout_workspace_bytes(int64_t A, int32_t E) {
+  LayoutGeom g = layout_geom(A);
+  return (size_t)g.nc * (size_t)(E > 0 ? E : 0) * sizeof(int32_t);
+}
+
+}  // namespace mxq

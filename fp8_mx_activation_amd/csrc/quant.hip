@@ -1,0 +1,195 @@
+// moe_scatter_quant, mx_quant_live_rows and the e4m3 codec check.
+//
+// Quantization follows sglang PR #33128 (implementation breakdown item 3:
+// quantize activations with a UE8M0 scale computed directly, fused with the
+// scatter) and sglang PR #36119 (implementation breakdown item 1: one e8m0
+// byte per 32 channels, quantized on the sender over live rows only).
+//
+// Work split: one block per token row (scatter) or per live row (send side);
+// a lane owns 16 consecutive channels, so one row is read once with 16-byte
+// loads, its group exponents come from in-wavefront max reductions, and the
+// 16 fp8 bytes a lane produces go to every destination row with one 16-byte
+// store each.  The scatter path is bandwidth-bound: per token it reads 2H
+// bytes and writes K*(H + H/G) bytes.
+#include "mxq_device.hpp"
+#include "mxq_host.hpp"
+
+namespace {
+
+using namespace mxq;
+
+// One block per token.  Destinations come from src2dst (uniform per block,
+// so they are scalar loads); a token without a destination in [0, num_rows)
+// is skipped before its row is read.
+template <int G>
+__global__ __launch_bounds__(1024) void scatter_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, int32_t H,
+    const int32_t* __restrict__ src2dst, int32_t K, uint8_t* __restrict__ q,
+    int64_t ld_q, uint8_t* __restrict__ s, int64_t ld_s, int64_t num_rows) {
+  const int64_t t = blockIdx.x;
+  const int32_t* dl = src2dst + t * K;
+  bool any = false;
+  for (int j = 0; j < K; ++j) {
+    const int64_t d = dl[j];
+    any |= (d >= 0 && d < num_rows);
+  }
+  if (!any) return;
+  const uint16_t* xr = x + t * ld_x;
+  const bool lead = (threadIdx.x & (G / 16 - 1)) == 0;
+  for (int col = threadIdx.x * 16; col < H; col += blockDim.x * 16) {
+    const u32x4 a = load16(xr + col);
+    const u32x4 b = load16(xr + col + 8);
+    int e;
+    const u32x4 v = quant16<G>(a, b, e);
+    const uint8_t sb = (uint8_t)(e + 127);
+    for (int j = 0; j < K; ++j) {
+      const int64_t d = dl[j];
+      if (d < 0 || d >= num_rows) continue;
+      store16(q + d * ld_q + col, v);
+      if (lead) s[d * ld_s + col / G] = sb;
+    }
+  }
+}
+
+// Send-side quant.  Segment g owns blocks [g*bps, (g+1)*bps); block i of a
+// segment handles its live rows i, i + bps, ...  The grid depends only on the
+// host arguments; blocks past the live count return at once.
+template <int G>
+__global__ __launch_bounds__(1024) void live_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, int64_t rps, int32_t bps,
+    const int32_t* __restrict__ live, int32_t H, uint8_t* __restrict__ q,
+    int64_t ld_q, uint8_t* __restrict__ s, int64_t ld_s) {
+  const int32_t g = blockIdx.x / bps;
+  const int32_t i = blockIdx.x - g * bps;
+  int64_t n = live[g];
+  n = n < 0 ? 0 : (n > rps ? rps : n);
+  const bool lead = (threadIdx.x & (G / 16 - 1)) == 0;
+  for (int64_t r = i; r < n; r += bps) {
+    const int64_t row = (int64_t)g * rps + r;
+    const uint16_t* xr = x + row * ld_x;
+    for (int col = threadIdx.x * 16; col < H; col += blockDim.x * 16) {
+      const u32x4 a = load16(xr + col);
+      const u32x4 b = load16(xr + col + 8);
+      int e;
+      const u32x4 v = quant16<G>(a, b, e);
+      store16(q + row * ld_q + col, v);
+      if (lead) s[row * ld_s + col / G] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void encode_e4m3_kernel(
+    const float* __restrict__ in, int64_t n, uint8_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n;
+       i += stride) {
+    if (i + 4 <= n) {
+      const uint32_t w = pack4_e4m3(in[i], in[i + 1], in[i + 2], in[i + 3]);
+      out[i] = (uint8_t)w;
+      out[i + 1] = (uint8_t)(w >> 8);
+      out[i + 2] = (uint8_t)(w >> 16);
+      out[i + 3] = (uint8_t)(w >> 24);
+    } else {
+      for (int64_t k = i; k < n; ++k)
+        out[k] = (uint8_t)pack4_e4m3(in[k], 0.f, 0.f, 0.f);
+    }
+  }
+}
+
+bool rows_ok_bf16(const void* p, int64_t ld) {
+  return aligned16(p) && (ld * 2) % 16 == 0;
+}
+bool rows_ok_u8(const void* p, int64_t ld) {
+  return aligned16(p) && ld % 16 == 0;
+}
+
+}  // namespace
+
+extern "C" mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x,
+                                        int64_t T, int32_t H,
+                                        const int32_t* src2dst, int32_t K,
+                                        mxq_scale_fmt fmt, void* q_fp8,
+                                        int64_t ld_q, uint8_t* scales,
+                                        int64_t ld_s, int64_t num_rows,
+                                        void* stream) {
+  const int G = group_of(fmt);
+  if (G == 0) return MXQ_ERR_UNSUPPORTED;
+  if (T < 0 || T > INT32_MAX || H <= 0 || H % G != 0 || K < 0 ||
+      K > MXQ_MAX_TOPK || num_rows < 0 || num_rows > INT32_MAX)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (T == 0 || K == 0) return MXQ_OK;
+  if (x_bf16 == nullptr || src2dst == nullptr || ld_x < H)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (num_rows > 0 && (q_fp8 == nullptr || scales == nullptr))
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (ld_q < H || ld_s < H / G) return MXQ_ERR_INVALID_ARGUMENT;
+  if (!rows_ok_bf16(x_bf16, ld_x) || (num_rows > 0 && !rows_ok_u8(q_fp8, ld_q)))
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (num_rows == 0) return MXQ_OK;
+
+  const int threads = row_block_threads(H, 16);
+  hipStream_t s = as_stream(stream);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* q = static_cast<uint8_t*>(q_fp8);
+  if (G == 128)
+    scatter_quant_kernel<128><<<(unsigned)T, threads, 0, s>>>(
+        x, ld_x, H, src2dst, K, q, ld_q, scales, ld_s, num_rows);
+  else
+    scatter_quant_kernel<32><<<(unsigned)T, threads, 0, s>>>(
+        x, ld_x, H, src2dst, K, q, ld_q, scales, ld_s, num_rows);
+  return launch_status();
+}
+
+extern "C" mxq_status mx_quant_live_rows(const void* x_bf16, int64_t ld_x,
+                                         int32_t num_segments,
+                                         int64_t rows_per_segment,
+                                         const int32_t* live_counts, int32_t H,
+                                         mxq_scale_fmt fmt, void* q_fp8,
+                                         int64_t ld_q, uint8_t* scales,
+                                         int64_t ld_s, void* stream) {
+  const int G = group_of(fmt);
+  if (G == 0) return MXQ_ERR_UNSUPPORTED;
+  if (num_segments < 0 || rows_per_segment < 0 || H <= 0 || H % G != 0)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (num_segments == 0 || rows_per_segment == 0) return MXQ_OK;
+  if ((int64_t)num_segments * rows_per_segment > INT32_MAX)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (x_bf16 == nullptr || live_counts == nullptr || q_fp8 == nullptr ||
+      scales == nullptr)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (ld_x < H || ld_q < H || ld_s < H / G) return MXQ_ERR_INVALID_ARGUMENT;
+  if (!rows_ok_bf16(x_bf16, ld_x) || !rows_ok_u8(q_fp8, ld_q))
+    return MXQ_ERR_INVALID_ARGUMENT;
+
+  // About 1024 blocks in all, at most one per padded row of a segment.
+  int64_t bps = ceil_div(1024, num_segments);
+  if (bps > rows_per_segment) bps = rows_per_segment;
+  if (bps < 1) bps = 1;
+  const int64_t blocks = bps * num_segments;
+  if (blocks > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
+  const int threads = row_block_threads(H, 16);
+  hipStream_t s = as_stream(stream);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* q = static_cast<uint8_t*>(q_fp8);
+  if (G == 32)
+    live_rows_kernel<32><<<(unsigned)blocks, threads, 0, s>>>(
+        x, ld_x, rows_per_segment, (int32_t)bps, live_counts, H, q, ld_q,
+        scales, ld_s);
+  else
+    live_rows_kernel<128><<<(unsigned)blocks, threads, 0, s>>>(
+        x, ld_x, rows_per_segment, (int32_t)bps, live_counts, H, q, ld_q,
+        scales, ld_s);
+  return launch_status();
+}
+
+extern "C" mxq_status mxq_e4m3_encode_f32(const float* in, int64_t n,
+                                          uint8_t* out, void* stream) {
+  if (n < 0) return MXQ_ERR_INVALID_ARGUMENT;
+  if (n == 0) return MXQ_OK;
+  if (in == nullptr || out == nullptr) return MXQ_ERR_INVALID_ARGUMENT;
+  int64_t blocks = ceil_div(ceil_div(n, 4), 256);
+  if (blocks > 16384) blocks = 16384;
+  encode_e4m3_kernel<<<(unsigned)blocks, 256, 0, as_stream(stream)>>>(in, n,
+                                                                       out);
+  return launch_status();
+}

@@ -1,0 +1,162 @@
+// requant_per_token_to_per_tensor: fp8 rows with one fp32 scale per token ->
+// fp8 rows with one fp32 scale for the whole tensor, so a low-latency
+// dispatch can move fp8 instead of bf16 (sglang PR #14162, implementation
+// breakdown items 1-2).
+//
+// Two launches with static grids:
+//   requant_amax_kernel   kPartials blocks; a wavefront takes whole rows, gets
+//                         the row's largest magnitude byte with packed 16-bit
+//                         max operations and a wavefront max, decodes it and
+//                         multiplies by the token scale; each block writes the
+//                         max of its rows (fp32 bits of a non-negative float
+//                         order like unsigned integers) to workspace.
+//   requant_apply_kernel  every block reduces the partials (a few KB from
+//                         L2), forms S = amax / 448 and 1 / S with IEEE
+//                         division, then rewrites its rows:
+//                         q' = e4m3((dec(q) * s_t) * (1 / S)).
+// The input is read twice; at 16384 x 4096 it is 64 MiB, which the 256 MB
+// last-level cache of MI355X holds between the two passes.
+#include "mxq_device.hpp"
+#include "mxq_host.hpp"
+
+namespace {
+
+using namespace mxq;
+
+constexpr int kPartials = 512;
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Largest magnitude byte (sign bit cleared) of 16 e4m3 bytes.
+__device__ __forceinline__ uint32_t mag_max16(const u32x4& v) {
+  u16x2 m = {0, 0};
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u16x2 ev = __builtin_bit_cast(u16x2, w[i] & 0x007F007Fu);
+    const u16x2 od = __builtin_bit_cast(u16x2, (w[i] >> 8) & 0x007F007Fu);
+    m = __builtin_elementwise_max(m, __builtin_elementwise_max(ev, od));
+  }
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+__device__ __forceinline__ uint32_t requant4(uint32_t w, float st, float inv) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return pack4_e4m3((lo[0] * st) * inv, (lo[1] * st) * inv,
+                    (hi[0] * st) * inv, (hi[1] * st) * inv);
+}
+
+__global__ __launch_bounds__(256) void requant_amax_kernel(
+    const uint8_t* __restrict__ q, int64_t ld, const float* __restrict__ sc,
+    int64_t T, int32_t H, uint32_t* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int64_t H16 = (int64_t)(H / 16) * 16;
+  uint32_t best = 0;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wv; row < T;
+       row += (int64_t)gridDim.x * 4) {
+    const uint8_t* r = q + row * ld;
+    uint32_t m = 0;
+    for (int64_t col = lane * 16; col < H16; col += 64 * 16)
+      m = max(m, mag_max16(load16(r + col)));
+    for (int64_t col = H16 + lane; col < H; col += 64)
+      m = max(m, (uint32_t)(r[col] & 0x7F));
+    m = wave_max(m);
+    const float rq = __builtin_amdgcn_cvt_f32_fp8((int)m, 0) * sc[row];
+    best = max(best, __float_as_uint(rq));
+  }
+  __shared__ uint32_t red[4];
+  best = wave_max(best);
+  if (lane == 0) red[wv] = best;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    partial[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// q_in and q_out may be the same buffer: every byte is read and then written
+// by the same lane.
+__global__ __launch_bounds__(256) void requant_apply_kernel(
+    const uint8_t* q_in, int64_t ld_in, const float* __restrict__ sc,
+    int64_t T, int32_t H, uint8_t* q_out, int64_t ld_out,
+    const uint32_t* __restrict__ partial, int32_t np,
+    float* __restrict__ tensor_scale) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  __shared__ uint32_t red[4];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < np; i += 256) m = max(m, partial[i]);
+  m = wave_max(m);
+  if (lane == 0) red[wv] = m;
+  __syncthreads();
+  const float amax = __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])));
+  const float S = amax > 0.0f ? amax / 448.0f : 1.0f;
+  const float inv = 1.0f / S;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = S;
+
+  const int64_t H16 = (int64_t)(H / 16) * 16;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wv; row < T;
+       row += (int64_t)gridDim.x * 4) {
+    const float st = sc[row];
+    const uint8_t* ri = q_in + row * ld_in;
+    uint8_t* ro = q_out + row * ld_out;
+    for (int64_t col = lane * 16; col < H16; col += 64 * 16) {
+      const u32x4 v = load16(ri + col);
+      u32x4 o;
+      o.x = requant4(v.x, st, inv);
+      o.y = requant4(v.y, st, inv);
+      o.z = requant4(v.z, st, inv);
+      o.w = requant4(v.w, st, inv);
+      store16(ro + col, o);
+    }
+    for (int64_t col = H16 + lane; col < H; col += 64)
+      ro[col] = (uint8_t)requant4(ri[col], st, inv);
+  }
+}
+
+}  // namespace
+
+extern "C" size_t requant_workspace_bytes(int64_t T, int32_t H) {
+  (void)T;
+  (void)H;
+  return kPartials * sizeof(uint32_t);
+}
+
+extern "C" mxq_status requant_per_token_to_per_tensor(
+    const void* q_in_fp8, int64_t ld_in, const float* token_scales, int64_t T,
+    int32_t H, void* q_out_fp8, int64_t ld_out, float* tensor_scale,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 0 || H <= 0 || tensor_scale == nullptr)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (T > 0) {
+    if (q_in_fp8 == nullptr || q_out_fp8 == nullptr || token_scales == nullptr)
+      return MXQ_ERR_INVALID_ARGUMENT;
+    if (ld_in < H || ld_out < H) return MXQ_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q_in_fp8) || ld_in % 16 != 0 || !aligned16(q_out_fp8) ||
+        ld_out % 16 != 0)
+      return MXQ_ERR_INVALID_ARGUMENT;
+    if (q_in_fp8 == q_out_fp8 && ld_in != ld_out)
+      return MXQ_ERR_INVALID_ARGUMENT;
+  }
+  if (workspace == nullptr || workspace_bytes < requant_workspace_bytes(T, H))
+    return MXQ_ERR_WORKSPACE;
+
+  hipStream_t s = as_stream(stream);
+  uint32_t* partial = static_cast<uint32_t*>(workspace);
+  int64_t np = ceil_div(T, 4);
+  if (np > kPartials) np = kPartials;
+  if (np > 0) {
+    requant_amax_kernel<<<(unsigned)np, 256, 0, s>>>(
+        static_cast<const uint8_t*>(q_in_fp8), ld_in, token_scales, T, H,
+        partial);
+    if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;
+  }
+  int64_t blocks = ceil_div(T, 8);
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  requant_apply_kernel<<<(unsigned)blocks, 256, 0, s>>>(
+      static_cast<const uint8_t*>(q_in_fp8), ld_in, token_scales, T, H,
+      static_cast<uint8_t*>(q_out_fp8), ld_out, partial, (int32_t)np,
+      tensor_scale);
+  return launch_status();
+}

@@ -1,0 +1,235 @@
+/*
+ * mxq.h - MoE expert-dispatch preprocessing with fp8 e4m3 activations and
+ * power-of-two group scales, for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libmxq.so.  Every entry point takes plain pointers and sizes.
+ *
+ * Sources (summaries of sglang pull requests):
+ *   [P1] sglang PR #33128 page - DeepGEMM under the standard MoE dispatcher:
+ *        compact layout with a static row bound, -1 expert index on padding
+ *        rows, direct UE8M0 activation quant.
+ *   [P2] sglang PR #14162 page - DeepEP low-latency dispatch in fp8: a
+ *        per-token -> per-tensor fp8 requant step.
+ *   [P3] sglang PR #29525 page - DeepEPv2 backend: psum (block-aligned)
+ *        layout, masked slab [E, max_m, hidden] with masked_m, fused top-k
+ *        weights on real rows only, fail-fast overflow.
+ *   [P4] sglang PR #36119 page - MXFP8 dispatch on MI355X: send-side quant
+ *        over live tokens, one e8m0 byte per 32 channels (224 at hidden 7168).
+ *
+ * Conventions shared by every call:
+ *   - Device pointers are HIP device memory; "host" marks the exceptions.
+ *     The caller owns every buffer.  The library allocates nothing and keeps
+ *     no state between calls, so calls are re-entrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it and returns without waiting, except
+ *     moe_read_overflow, which waits for the stream.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     failed check returns MXQ_ERR_INVALID_ARGUMENT (or MXQ_ERR_UNSUPPORTED
+ *     for a format or size the library does not implement, MXQ_ERR_WORKSPACE
+ *     for a short workspace) and enqueues nothing.  MXQ_ERR_HIP means a kernel
+ *     launch was rejected by the runtime.
+ *   - Launch geometry depends only on the host arguments, never on device
+ *     data, so every call can be captured in a hipGraph and replayed.
+ *   - Row offsets are 64-bit internally; row indices stored in int32 arrays
+ *     limit a layout to 2^31 - 1 rows.
+ *   - bf16 = bfloat16 (upper half of an IEEE binary32).  fp8 = OCP e4m3fn
+ *     (bias 7, largest finite 448, no infinities).  A scale byte b means the
+ *     factor 2^(b - 127) (UE8M0 / e8m0).
+ *   - Vector rows: bf16 and fp8 row starts must be 16-byte aligned (base
+ *     pointer 16-byte aligned, row stride a multiple of 16 bytes).
+ *   - Inputs are finite; NaN or infinite activations give unspecified bytes.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+#define MXQ_MAX_LOCAL_EXPERTS 1024
+#define MXQ_MAX_TOPK 64
+
+typedef enum {
+  MXQ_OK = 0,
+  MXQ_ERR_INVALID_ARGUMENT = 1,
+  MXQ_ERR_UNSUPPORTED = 2,
+  MXQ_ERR_CAPACITY_OVERFLOW = 3,
+  MXQ_ERR_WORKSPACE = 4,
+  MXQ_ERR_HIP = 5
+} mxq_status;
+
+typedef enum { MXQ_LAYOUT_COMPACT = 0, MXQ_LAYOUT_MASKED = 1 } mxq_layout_kind;
+
+/* Both formats store one byte per group meaning 2^(b-127); the exponent is
+ * the smallest e with amax(group) <= 448 * 2^e, clamped to [-127, 127]. */
+typedef enum {
+  MXQ_SCALE_UE8M0_G128 = 0, /* 128 channels per scale [P1 impl. item 3] */
+  MXQ_SCALE_E8M0_G32 = 1    /* 32 channels per scale  [P4 impl. item 1] */
+} mxq_scale_fmt;
+
+typedef enum { MXQ_OUT_BF16 = 0, MXQ_OUT_F32 = 1 } mxq_out_dtype;
+
+/* ------------------------------------------------------------ host-only */
+
+/* Static row count of the compact layout that no routing can exceed
+ * [P1 Key source snippets, _get_compact_all_tokens]:
+ *   block_e * (n + (A - n) / block_e), n = min(A, E).
+ * Pure host function.  Returns -1 if an argument is negative or block_e < 1. */
+int64_t moe_compact_row_bound(int64_t num_assignments,
+                              int32_t num_local_experts, int32_t block_e);
+
+/* Layout choice [P1 Key source snippets, _should_use_masked_standard_layout]:
+ * 1 (masked slab) iff num_experts > num_local_experts and
+ * num_local_experts <= 32, else 0 (compact).  Pure host function. */
+int32_t moe_should_use_masked(int32_t num_experts, int32_t num_local_experts);
+
+/* Workspace bytes moe_layout needs for T tokens, top-K, E local experts. */
+size_t moe_layout_workspace_bytes(int64_t T, int32_t K, int32_t E);
+
+/* Workspace bytes requant_per_token_to_per_tensor needs. */
+size_t requant_workspace_bytes(int64_t T, int32_t H);
+
+/* ----------------------------------------------------------------- layout */
+
+/* Lay top-k routing out by expert [P1 impl. items 2-3 and Key source snippets
+ * (_fwd_kernel_ep_scatter_1); P3 impl. items 2-3 (masked slab, masked_m)].
+ *
+ *   topk_ids      int32 [T, K] row-major, global expert ids.  Assignment
+ *                 (t, j) is local iff e = topk_ids[t*K+j] - expert_begin lies
+ *                 in [0, num_local_experts).
+ *   kind          MXQ_LAYOUT_COMPACT: expert e owns rows
+ *                   [expert_offsets[e], expert_offsets[e+1]) whose length is
+ *                   ceil(c_e / block_e) * block_e (0 for an empty expert),
+ *                   regions in ascending e.  num_rows must be at least
+ *                   moe_compact_row_bound(T*K, E, block_e).
+ *                 MXQ_LAYOUT_MASKED: expert e owns rows [e*capacity,
+ *                   (e+1)*capacity); num_rows must be >= E*capacity.
+ *   Slots: the i-th local assignment of expert e in ascending flat index
+ *   t*K+j gets row expert_offsets[e] + i (deterministic).
+ *
+ * Outputs (all written by every call; no prior clearing needed):
+ *   counts         int32 [E]    c_e, the local assignments of expert e.
+ *   expert_offsets int32 [E+1]  region starts; [E] = end of the last region.
+ *   m_indices      int32 [num_rows] or NULL: e on rows holding an assignment
+ *                  of e, -1 on every other row (padding and tail rows).
+ *   masked_m       int32 [E] or NULL: min(c_e, capacity) (masked) or c_e.
+ *   src2dst        int32 [T, K]: destination row, -1 for a non-local
+ *                  assignment or (masked) a slot >= capacity.
+ *   overflow_flag  int32 [1]: 1 if some expert exceeded the slab capacity
+ *                  (masked), else 0.  Overflowing assignments are dropped,
+ *                  never written out of bounds; read with moe_read_overflow.
+ *   workspace      >= moe_layout_workspace_bytes(T, K, E) bytes, device.
+ * Limits: 1 <= E <= MXQ_MAX_LOCAL_EXPERTS, 1 <= K <= MXQ_MAX_TOPK,
+ * T*K < 2^31, num_rows < 2^31.  T = 0 is valid (regions empty, m_indices all
+ * -1). */
+mxq_status moe_layout(const int32_t* topk_ids, int64_t T, int32_t K,
+                      int32_t expert_begin, int32_t num_local_experts,
+                      mxq_layout_kind kind, int32_t block_e, int32_t capacity,
+                      int64_t num_rows, int32_t* counts,
+                      int32_t* expert_offsets, int32_t* m_indices,
+                      int32_t* masked_m, int32_t* src2dst,
+                      int32_t* overflow_flag, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Host read of the overflow flag written by moe_layout.  Waits for `stream`.
+ * host_value (host) receives the flag; returns MXQ_ERR_CAPACITY_OVERFLOW if
+ * it is set, MXQ_OK otherwise [P3 Review highlights: overflow fails fast]. */
+mxq_status moe_read_overflow(const int32_t* overflow_flag, int32_t* host_value,
+                             void* stream);
+
+/* ---------------------------------------------------------- scatter + quant */
+
+/* Quantize each token row once and scatter it to its destination rows
+ * [P1 impl. item 3: fused quant + scatter with UE8M0 scales computed
+ * directly; P1 Key source snippets].
+ *
+ *   x        bf16 [T, ld_x] device, the first H columns of each row are used.
+ *   src2dst  int32 [T, K] from moe_layout (either kind); entries < 0 or
+ *            >= num_rows are skipped.
+ *   fmt      group size and scale format.  H must be a multiple of the group.
+ *   q        fp8 [num_rows, ld_q]; for every destination row d of token t the
+ *            first H bytes become e4m3(x[t, i] * 2^-e_g).
+ *   scales   uint8 [num_rows, ld_s]; byte g of row d becomes e_g + 127,
+ *            ld_s >= H / G (any stride, padded strides allowed).
+ * Rows that are no destination are not written (padding keeps whatever the
+ * caller left there; consumers skip them through m_indices = -1). */
+mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x, int64_t T,
+                             int32_t H, const int32_t* src2dst, int32_t K,
+                             mxq_scale_fmt fmt, void* q_fp8, int64_t ld_q,
+                             uint8_t* scales, int64_t ld_s, int64_t num_rows,
+                             void* stream);
+
+/* Send-side quant over live rows only [P4 Features & motivation and impl.
+ * item 1: quantize on the sender over the live tokens, not the padded
+ * receive buffer; 224 one-byte scales per 7168-wide row].
+ *
+ *   x            bf16 [num_segments * rows_per_segment, ld_x].
+ *   live_counts  int32 [num_segments] device: segment g's live rows are
+ *                [g*rows_per_segment, g*rows_per_segment + live_counts[g]);
+ *                counts are clipped to [0, rows_per_segment].
+ *   q, scales    same layout as the input rows; only live rows are written.
+ * The grid is sized from the host arguments; blocks beyond the live rows
+ * return at once. */
+mxq_status mx_quant_live_rows(const void* x_bf16, int64_t ld_x,
+                              int32_t num_segments, int64_t rows_per_segment,
+                              const int32_t* live_counts, int32_t H,
+                              mxq_scale_fmt fmt, void* q_fp8, int64_t ld_q,
+                              uint8_t* scales, int64_t ld_s, void* stream);
+
+/* ------------------------------------------------------------- requant */
+
+/* Per-token scaled fp8 -> one per-tensor scale [P2 impl. items 1-2].
+ *
+ *   q_in          fp8 [T, ld_in]; token_scales fp32 [T] (positive, finite).
+ *   q_out         fp8 [T, ld_out]; may equal q_in when ld_out == ld_in.
+ *   tensor_scale  fp32 [1] device: S = fl(amax / 448) where
+ *                 amax = max_t fl(max_i |dec(q_in[t,i])| * s_t); S = 1 when
+ *                 amax = 0.  q_out = e4m3(fl(fl(dec(q_in) * s_t) * fl(1/S))).
+ *   workspace     >= requant_workspace_bytes(T, H) bytes, device.
+ * Two kernels: a max pass, then the requant pass. */
+mxq_status requant_per_token_to_per_tensor(
+    const void* q_in_fp8, int64_t ld_in, const float* token_scales, int64_t T,
+    int32_t H, void* q_out_fp8, int64_t ld_out, float* tensor_scale,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------- combine */
+
+/* Un-permute expert outputs to tokens with the top-k weights [P1 impl. item 2
+ * and Risks item 2 (post-permute through src2dst); P3 impl. item 3 (top-k
+ * weights fused on real rows only)].
+ *
+ *   y             bf16 [num_rows, ld_y] expert outputs in layout order.
+ *   src2dst       int32 [T, K]; entries < 0 or >= num_rows are skipped, so
+ *                 padding rows are never read.
+ *   topk_weights  fp32 [T, K].
+ *   out           [T, ld_out], bf16 or fp32 per out_dtype:
+ *                 acc = +0; for j = 0..K-1 with a valid row:
+ *                 acc = fma(w[t,j], y[row, i], acc); out = acc rounded to
+ *                 nearest-even bf16, or acc itself for fp32.
+ * H must be a multiple of 8. */
+mxq_status moe_combine(const void* y_bf16, int64_t ld_y, int64_t num_rows,
+                       const int32_t* src2dst, const float* topk_weights,
+                       int64_t T, int32_t K, int32_t H, void* out,
+                       int64_t ld_out, mxq_out_dtype out_dtype, void* stream);
+
+/* ---------------------------------------------------------- diagnostics */
+
+/* The fp32 -> e4m3fn conversion every kernel above uses, exposed so it can
+ * be checked value by value (OCP e4m3fn, nearest-even).  Defined for
+ * |x| < 464; larger inputs are outside the contract of the quant kernels,
+ * which never produce them.  in fp32 [n], out uint8 [n], device. */
+mxq_status mxq_e4m3_encode_f32(const float* in, int64_t n, uint8_t* out,
+                               void* stream);
+
+const char* mxq_status_string(mxq_status s);
+int32_t mxq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -1,0 +1,160 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/mxq.h declares, its host-only helpers agree with the oracle,
+and argument validation rejects bad calls before anything is enqueued (no
+compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 4
+
+
+@pytest.fixture(scope="module")
+def mxq():
+    import fp8_mx_activation_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from fp8_mx_activation_amd import build
+        build.build(verbose=False)
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_path(mxq):
+    names = declared_functions()
+    for n in ("moe_layout", "moe_scatter_quant", "mx_quant_live_rows",
+              "requant_per_token_to_per_tensor", "moe_combine",
+              "moe_compact_row_bound", "moe_should_use_masked",
+              "moe_read_overflow", "mxq_e4m3_encode_f32"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(mxq):
+    L = ctypes.CDLL(mxq.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) <= set(mxq._SIGNATURES)
+
+
+def test_abi_version_and_status_strings(mxq):
+    assert mxq.mxq_abi_version() == 1
+    L = mxq.lib()
+    assert L.mxq_status_string(0) == b"ok"
+    assert b"capacity" in L.mxq_status_string(3)
+
+
+def test_host_helpers_match_oracle(mxq, ora):
+    for A, E, b in [(128, 8, 128), (65536, 256, 128), (131072, 128, 128),
+                    (0, 3, 128), (7, 9, 4), (1000, 1, 1)]:
+        assert mxq.moe_compact_row_bound(A, E, b) == \
+            ora.compact_row_bound(A, E, b)
+    for g, l in [(256, 32), (256, 256), (256, 33), (8, 8), (64, 8)]:
+        assert mxq.moe_should_use_masked(g, l) == ora.should_use_masked(g, l)
+    assert mxq.lib().moe_compact_row_bound(-1, 8, 128) == -1
+    assert mxq.lib().moe_compact_row_bound(8, 8, 0) == -1
+
+
+def test_workspace_sizes(mxq):
+    assert mxq.moe_layout_workspace_bytes(0, 8, 256) == 0
+    w = mxq.moe_layout_workspace_bytes(8192, 8, 256)
+    assert 0 < w <= 64 * 256 * 4
+    assert mxq.requant_workspace_bytes(16384, 4096) >= 4
+
+
+FAKE = 0x10000  # a 16-byte aligned non-null pointer value; never dereferenced
+
+
+def test_scatter_quant_validation(mxq):
+    L = mxq.lib()
+    ok = dict(x=FAKE, ld_x=256, T=4, H=256, s2d=FAKE, K=2, fmt=0, q=FAKE,
+              ld_q=256, s=FAKE, ld_s=2, rows=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.moe_scatter_quant(a["x"], a["ld_x"], a["T"], a["H"],
+                                   a["s2d"], a["K"], a["fmt"], a["q"],
+                                   a["ld_q"], a["s"], a["ld_s"], a["rows"],
+                                   None)
+
+    assert call(fmt=7) == UNSUPPORTED
+    assert call(H=200) == INVALID              # not a multiple of 128
+    assert call(H=96, fmt=1, ld_s=2) == INVALID  # 3 scales need ld_s >= 3
+    assert call(ld_q=128) == INVALID
+    assert call(ld_x=100) == INVALID
+    assert call(s=None) == INVALID             # missing scales, rows > 0
+    assert call(x=FAKE + 8) == INVALID         # misaligned rows
+    assert call(ld_q=264) == INVALID           # fp8 stride not 16-byte
+    assert call(T=-1) == INVALID
+    assert call(K=65) == INVALID
+    assert call(T=0) == 0                      # empty batch: nothing to do
+    assert call(rows=0, q=None, s=None) == 0
+
+
+def test_layout_validation(mxq):
+    L = mxq.lib()
+
+    def call(T=8, K=2, E=4, kind=0, block=128, cap=0, rows=None, ws=FAKE,
+             wsb=1 << 20, ids=FAKE):
+        if rows is None:
+            rows = mxq.moe_compact_row_bound(T * K, E, block)
+        return L.moe_layout(ids, T, K, 0, E, kind, block, cap, rows, FAKE,
+                            FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+
+    assert call(rows=100) == INVALID           # below the compact bound
+    assert call(E=0) == INVALID
+    assert call(E=1025) == INVALID
+    assert call(K=0) == INVALID
+    assert call(kind=5) == UNSUPPORTED
+    assert call(kind=1, cap=0, rows=0) == INVALID
+    assert call(kind=1, cap=16, rows=63) == INVALID  # E * cap = 64
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=4) == WORKSPACE
+    assert call(ids=None) == INVALID
+    assert call(block=0, rows=1024) == INVALID
+
+
+def test_combine_requant_live_validation(mxq):
+    L = mxq.lib()
+    assert L.moe_combine(FAKE, 256, 16, FAKE, FAKE, 4, 2, 260, FAKE, 260, 0,
+                         None) == INVALID     # H % 8
+    assert L.moe_combine(FAKE, 256, 16, FAKE, FAKE, 4, 2, 256, FAKE, 256, 9,
+                         None) == UNSUPPORTED
+    assert L.moe_combine(FAKE, 256, 16, FAKE, FAKE, 0, 2, 256, FAKE, 256, 0,
+                         None) == 0
+    assert L.requant_per_token_to_per_tensor(FAKE, 256, FAKE, 4, 256, FAKE,
+                                             256, FAKE, None, 0,
+                                             None) == WORKSPACE
+    assert L.requant_per_token_to_per_tensor(FAKE, 256, FAKE, 4, 256, FAKE,
+                                             128, FAKE, FAKE, 4096,
+                                             None) == INVALID
+    assert L.requant_per_token_to_per_tensor(FAKE, 256, FAKE, 4, 256, FAKE,
+                                             256, None, FAKE, 4096,
+                                             None) == INVALID
+    assert L.mx_quant_live_rows(FAKE, 256, 2, 8, FAKE, 250, 1, FAKE, 256,
+                                FAKE, 8, None) == INVALID  # 250 % 32
+    assert L.mx_quant_live_rows(FAKE, 256, 0, 8, FAKE, 256, 1, FAKE, 256,
+                                FAKE, 8, None) == 0
+    assert L.mxq_e4m3_encode_f32(FAKE, -1, FAKE, None) == INVALID
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package imports neither the oracle nor the input generators."""
+    pkg = os.path.join(ROOT, "fp8_mx_activation_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+(oracle|"
+                                     r"synthetic_inputs)\b", src, re.M), f

@@ -1,0 +1,118 @@
+"""moe_layout on the GPU against the oracle: counts, region starts, src2dst,
+m_indices, masked_m and the overflow flag must match exactly."""
+import numpy as np
+import pytest
+
+import fp8_mx_activation_amd as mxq
+import synthetic_inputs as si
+from gpu_util import assert_equal, host, i32_to_dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_both(ora, ids, begin, E, kind, block_e=128, cap=0, num_rows=None,
+             m_indices=True):
+    ids = np.ascontiguousarray(ids, np.int32)
+    ref = ora.moe_layout(ids, begin, E, kind, block_e=block_e, capacity=cap,
+                         num_rows=num_rows)
+    say("layout", kind, "T=%d K=%d E=%d begin=%d block=%d cap=%d rows=%d"
+        % (ids.shape[0], ids.shape[1], E, begin, block_e, cap,
+           ref["num_rows"]))
+    got = mxq.moe_layout(i32_to_dev(ids), begin, E, kind, block_e=block_e,
+                         capacity=cap, num_rows=ref["num_rows"],
+                         m_indices=m_indices)
+    assert_equal(host(got["counts"]), ref["counts"], "counts")
+    assert_equal(host(got["expert_offsets"]), ref["expert_offsets"],
+                 "expert_offsets")
+    assert_equal(host(got["src2dst"]), ref["src2dst"], "src2dst")
+    if m_indices:
+        assert_equal(host(got["m_indices"]), ref["m_indices"], "m_indices")
+    assert_equal(host(got["masked_m"]), ref["masked_m"], "masked_m")
+    assert mxq.moe_read_overflow(got["overflow_flag"]) == ref["overflow"]
+    return got, ref
+
+
+def test_tiny(ora):
+    b = si.tiny()
+    run_both(ora, b.topk_ids, 0, 8, "compact")
+
+
+def test_decode_masked(ora):
+    b = si.decode_masked()
+    got, ref = run_both(ora, b.topk_ids, 0, 32, "masked", cap=128)
+    assert ref["overflow"] == 0
+
+
+def test_decode_as_compact(ora):
+    b = si.decode_masked()
+    run_both(ora, b.topk_ids, 0, 32, "compact")
+
+
+def test_prefill_compact_full(ora):
+    b = si.prefill_compact(H=128)   # routing only; H does not matter here
+    got, ref = run_both(ora, b.topk_ids, 0, 256, "compact")
+    assert ref["num_rows"] == 98048
+    assert (ref["counts"] == 0).any()          # Zipf tail leaves experts empty
+
+
+def test_large_combine_routing(ora):
+    ids, _ = si.large_combine_routing()
+    got, ref = run_both(ora, ids, 0, 128, "compact")
+    assert ref["num_rows"] == 147328
+
+
+def test_expert_window_and_nonlocal(ora):
+    rng = np.random.default_rng(1)
+    ids = si.uniform_topk(rng, 500, 256, 8)
+    run_both(ora, ids, 64, 32, "compact")
+    run_both(ora, ids, 224, 32, "masked", cap=64)
+    run_both(ora, np.full((33, 3), 999, np.int32), 0, 16, "compact")
+
+
+def test_masked_overflow_flag(ora):
+    T, cap = 300, 128
+    ids = np.zeros((T, 2), np.int32)
+    ids[:, 0] = 5
+    ids[:, 1] = np.arange(T) % 7 + 8
+    got, ref = run_both(ora, ids, 0, 16, "masked", cap=cap)
+    assert ref["overflow"] == 1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shapes(ora, seed):
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.choice([1, 2, 3, 17, 64, 255, 256, 1000, 1024]))
+    K = int(rng.integers(1, min(E, 12) + 1))
+    T = int(rng.choice([1, 7, 64, 65, 513, 4099]))
+    block = int(rng.choice([1, 3, 64, 128]))
+    ids = si.uniform_topk(rng, T, E, K)
+    run_both(ora, ids, 0, E, "compact", block_e=block)
+    run_both(ora, ids, 0, E, "masked", cap=int(rng.integers(1, 40)))
+
+
+def test_ragged_adjacent_experts(ora):
+    counts = [127, 129, 1, 255, 256, 0, 2, 128]
+    ids = np.concatenate([np.full(c, e) for e, c in enumerate(counts)])
+    ids = np.random.default_rng(0).permutation(ids).reshape(-1, 1)
+    run_both(ora, ids, 0, len(counts), "compact")
+
+
+def test_spare_rows_and_no_m_indices(ora):
+    b = si.tiny()
+    run_both(ora, b.topk_ids, 0, 8, "compact", num_rows=1024 + 300)
+    run_both(ora, b.topk_ids, 0, 8, "masked", cap=20, num_rows=8 * 20 + 5)
+    run_both(ora, b.topk_ids, 0, 8, "compact", m_indices=False)
+
+
+def test_empty_batch(ora):
+    ids = np.zeros((0, 8), np.int32)
+    got, ref = run_both(ora, ids, 0, 256, "compact")
+    got, ref = run_both(ora, ids, 0, 32, "masked", cap=128)
+    assert (host(got["m_indices"]) == -1).all()
+
+
+def test_many_assignments(ora):
+    """Two million assignments: 64 chunks of 32768, long in-chunk walks."""
+    rng = np.random.default_rng(9)
+    ids = si.zipf_topk(rng, 262144, 256, 8)
+    run_both(ora, ids, 0, 256, "compact")
