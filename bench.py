@@ -1,0 +1,401 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE dispatch-preprocessing hot path on one MI355X.
+
+One step is one pass of the receive-side path over one prefill batch:
+moe_layout -> moe_scatter_quant -> moe_combine on T=8192 tokens,
+hidden 7168, 256 local experts, top-8 routing from a Zipf(1.1) expert
+popularity (8 experts never chosen), compact layout with 128-row blocks
+(98048-row static bound), fp8 e4m3 with UE8M0 group-128 scales.  Inputs are
+synthetic and already resident in HBM when the timed region starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line.  ``value`` is the step's algorithmic HBM bytes (what
+the method must move: each token row read once, each local assignment's fp8
+row and scales written once, each combined row read once, index and weight
+tables, no padding rows) divided by the measured step time.  Per-kernel
+times come from HIP events recorded on the stream the kernels run on.
+``cpu_baseline`` times the CPU oracle on the same workload on this host.
+The other rows of the path (masked decode slab, send-side live-row MX
+quant, per-token -> per-tensor requant, large combine) are timed separately
+under ``rows``; they are not part of ``value``.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("dispatch scatter+quant+combine HBM GB/s (% of MI355X peak); "
+          "assignments/sec")
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_prefill_traffic.txt")
+COMBINE_SRC = os.path.join(ROOT, "fp8_mx_activation_amd", "csrc",
+                           "combine.hip")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu", action="store_true",
+                   help="skip the CPU oracle baseline")
+    p.add_argument("--no-rows", action="store_true",
+                   help="skip the separately timed rows")
+    p.add_argument("--cpu-repeats", type=int, default=3)
+    return p.parse_args()
+
+
+# ------------------------------------------------------------ byte counts
+
+def bytes_layout(T, K, E, rows):
+    # ids read, src2dst written, m_indices written, counts + masked_m +
+    # region starts written
+    return T * K * 4 + T * K * 4 + rows * 4 + E * 8 + (E + 1) * 4
+
+
+def bytes_scatter(tokens_touched, T, K, H, G, assignments):
+    return tokens_touched * H * 2 + assignments * (H + H // G) + T * K * 4
+
+
+def bytes_combine(T, K, H, assignments, out_bytes=2):
+    return assignments * H * 2 + T * K * 8 + T * H * out_bytes
+
+
+# ---------------------------------------------------------------- helpers
+
+class EventTimer:
+    """HIP events recorded on the current stream (the one the library's
+    kernels are launched on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.torch.cuda.current_stream())
+        self.marks.append(e)
+        return e
+
+    @staticmethod
+    def ms(a, b):
+        return a.elapsed_time(b)
+
+
+def time_calls(torch, fn, reps=20, warmup=3):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    return float(np.median(per)) * 1e3  # microseconds
+
+
+def traffic_record():
+    """HBM bytes per combine launch from committed rocprofv3 counters, or
+    None if absent or taken on another version of the kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    src = hashlib.sha256(open(COMBINE_SRC, "rb").read()).hexdigest()
+    if kv.get("combine_source_sha256") != src:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write(
+            "bench.py runs on one GPU only: the path is measured on one GPU's "
+            "share of the experts at its real shape (--gpus 1); multi-GPU "
+            "runs are not part of this benchmark.\n")
+        sys.exit(2)
+
+    import torch
+
+    import fp8_mx_activation_amd as mxq
+    import synthetic_inputs as si
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------- inputs
+    b = si.prefill_compact()
+    T, H, K, E, G = b.T, b.H, b.K, b.n_local, b.group
+    R = mxq.moe_compact_row_bound(T * K, E, b.block_e)
+    x = torch.from_numpy(b.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    ids = torch.from_numpy(b.topk_ids).to(dev)
+    w = torch.from_numpy(b.topk_weights).to(dev)
+    y = si.gaussian_bf16_device(303, (R, H), dev)   # expert outputs
+    lay_out = {k: torch.empty(s, dtype=torch.int32, device=dev)
+               for k, s in (("counts", (E,)), ("expert_offsets", (E + 1,)),
+                            ("m_indices", (R,)), ("masked_m", (E,)),
+                            ("src2dst", (T, K)), ("overflow_flag", (1,)))}
+    ws = torch.empty(max(1, mxq.moe_layout_workspace_bytes(T, K, E)),
+                     dtype=torch.uint8, device=dev)
+    q = torch.empty((R, H), dtype=torch.uint8, device=dev)
+    s = torch.empty((R, H // G), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    local = ((b.topk_ids >= 0) & (b.topk_ids < E))
+    A = int(local.sum())
+    touched = int(local.any(axis=1).sum())
+    B_lay = bytes_layout(T, K, E, R)
+    B_sq = bytes_scatter(touched, T, K, H, G, A)
+    B_cb = bytes_combine(T, K, H, A)
+    B_step = B_lay + B_sq + B_cb
+
+    # box copy bandwidth (device-to-device copy, read + write bytes)
+    cbuf_a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cbuf_b = torch.empty_like(cbuf_a)
+    copy_us = time_calls(torch, lambda: cbuf_b.copy_(cbuf_a), reps=10)
+    copy_gbs = 2 * cbuf_a.numel() / (copy_us * 1e-6) / 1e9
+    del cbuf_a, cbuf_b
+
+    timer = EventTimer(torch)
+
+    def step(record):
+        if record:
+            timer.mark()
+        lay = mxq.moe_layout(ids, 0, E, "compact", num_rows=R, out=lay_out,
+                             workspace=ws)
+        if record:
+            timer.mark()
+        mxq.moe_scatter_quant(x, lay["src2dst"], R, "ue8m0_g128", q=q,
+                              scales=s)
+        if record:
+            timer.mark()
+        mxq.moe_combine(y, lay["src2dst"], w, out=out)
+        if record:
+            timer.mark()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    m = timer.marks
+    lay_ms = [m[4 * i].elapsed_time(m[4 * i + 1]) for i in range(args.steps)]
+    sq_ms = [m[4 * i + 1].elapsed_time(m[4 * i + 2])
+             for i in range(args.steps)]
+    cb_ms = [m[4 * i + 2].elapsed_time(m[4 * i + 3])
+             for i in range(args.steps)]
+    step_ms = wall_s * 1e3 / args.steps
+    ev_step_ms = float(np.mean(lay_ms) + np.mean(sq_ms) + np.mean(cb_ms))
+
+    value = B_step / (step_ms * 1e-3) / 1e9
+    cb_gbs = B_cb / (np.mean(cb_ms) * 1e-3) / 1e9
+    sq_gbs = B_sq / (np.mean(sq_ms) * 1e-3) / 1e9
+    sqcb_gbs = (B_sq + B_cb) / ((np.mean(sq_ms) + np.mean(cb_ms)) * 1e-3) / 1e9
+    traffic = traffic_record()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill compact dispatch: T=8192 tokens, hidden "
+                        "7168, 256 local experts, top-8 Zipf(1.1) routing "
+                        "(8 experts empty), compact layout block 128 "
+                        "(98048-row bound), fp8 e4m3 + UE8M0 group-128; "
+                        "step = moe_layout + moe_scatter_quant + moe_combine",
+            "tokens": T, "hidden": H, "local_experts": E, "topk": K,
+            "assignments": A, "layout_rows": R, "group": G,
+        },
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "assignments_per_s": round(A / (step_ms * 1e-3), 1),
+        "scatter_quant_plus_combine": {
+            "bytes": B_sq + B_cb,
+            "us": round(1e3 * (np.mean(sq_ms) + np.mean(cb_ms)), 2),
+            "gbs": round(sqcb_gbs, 2),
+            "pct_of_peak": round(100 * sqcb_gbs / PEAK_HBM_GBS, 2),
+        },
+        "kernels_us": {
+            "moe_layout": round(1e3 * float(np.mean(lay_ms)), 2),
+            "moe_scatter_quant": round(1e3 * float(np.mean(sq_ms)), 2),
+            "moe_combine": round(1e3 * float(np.mean(cb_ms)), 2),
+            "event_sum_per_step": round(1e3 * ev_step_ms, 2),
+        },
+        "kernels_gbs": {"moe_scatter_quant": round(sq_gbs, 2),
+                        "moe_combine": round(cb_gbs, 2)},
+        "algorithmic_bytes": {"moe_layout": B_lay, "moe_scatter_quant": B_sq,
+                              "moe_combine": B_cb, "step": B_step},
+        "box_copy_gbs": round(copy_gbs, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "moe_combine",
+            "achieved": round(cb_gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(cb_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    del q, s, out
+
+    if not args.no_rows:
+        result["rows"] = other_rows(torch, mxq, si, dev)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(torch, si, b, y, R, B_step,
+                                              args.cpu_repeats)
+    print(json.dumps(result), flush=True)
+
+
+# ------------------------------------------------- separately timed rows
+
+def other_rows(torch, mxq, si, dev):
+    rows = {}
+    # masked decode slab: one GPU's 32 of 256 experts, T=128
+    d = si.decode_masked()
+    ids = torch.from_numpy(d.topk_ids).to(dev)
+    x = torch.from_numpy(d.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(d.topk_weights).to(dev)
+    R = 32 * 128
+    q = torch.empty((R, d.H), dtype=torch.uint8, device=dev)
+    s = torch.empty((R, d.H // 128), dtype=torch.uint8, device=dev)
+    yv = si.gaussian_bf16_device(202, (R, d.H), dev)
+    lay = mxq.moe_layout(ids, 0, 32, "masked", capacity=128)
+    loc = int(((d.topk_ids >= 0) & (d.topk_ids < 32)).sum())
+    us_l = time_calls(torch, lambda: mxq.moe_layout(
+        ids, 0, 32, "masked", capacity=128, out=lay))
+    us_s = time_calls(torch, lambda: mxq.moe_scatter_quant(
+        x, lay["src2dst"], R, q=q, scales=s))
+    us_c = time_calls(torch, lambda: mxq.moe_combine(yv, lay["src2dst"], w))
+    rows["decode_masked"] = {
+        "workload": "T=128, hidden 7168, experts [0,32) of 256 local, top-8, "
+                    "slab capacity 128, UE8M0 group-128",
+        "local_assignments": loc, "layout_us": round(us_l, 2),
+        "scatter_quant_us": round(us_s, 2), "combine_us": round(us_c, 2),
+        "assignments_per_s": round(loc / ((us_l + us_s + us_c) * 1e-6), 1)}
+
+    # send-side MX quant over live rows: 24576 x 7168 padded, 112 live
+    xs = si.gaussian_bf16_device(404, (24576, 7168), dev)
+    qs = torch.empty((24576, 7168), dtype=torch.uint8, device=dev)
+    ss = torch.empty((24576, 224), dtype=torch.uint8, device=dev)
+    res = {}
+    for name, live in (("14x8", [14] * 8), ("112+0x7", [112] + [0] * 7),
+                       ("empty", [0] * 8)):
+        lc = torch.tensor(live, dtype=torch.int32, device=dev)
+        us = time_calls(torch, lambda: mxq.mx_quant_live_rows(
+            xs, 8, lc, q=qs, scales=ss))
+        n = sum(live)
+        byts = n * (7168 * 2 + 7168 + 224) + 32
+        res[name] = {"live_rows": n, "us": round(us, 2),
+                     "rows_per_s": round(n / (us * 1e-6), 1),
+                     "algorithmic_bytes": byts}
+    res["padded_grid_equivalent_bytes"] = 24576 * (7168 * 2 + 7168 + 224)
+    res["workload"] = ("24576 x 7168 bf16 padded buffer = 8 segments of "
+                       "3072 rows, e8m0 group-32 (224 scales/row)")
+    rows["live_rows_mx"] = res
+    del xs, qs, ss
+
+    # per-token -> per-tensor requant, 16384 x 4096
+    rb = si.requant_input()
+    qi = torch.from_numpy(rb.q).to(dev)
+    sc = torch.from_numpy(rb.scales).to(dev)
+    qo = torch.empty_like(qi)
+    Sd = torch.empty(1, dtype=torch.float32, device=dev)
+    rws = torch.empty(mxq.requant_workspace_bytes(*qi.shape),
+                      dtype=torch.uint8, device=dev)
+    us = time_calls(torch, lambda: mxq.requant_per_token_to_per_tensor(
+        qi, sc, q_out=qo, tensor_scale=Sd, workspace=rws))
+    byts = 2 * qi.numel() + qi.shape[0] * 4 + 4
+    rows["requant"] = {"workload": "16384 x 4096 fp8, per-token scales "
+                                   "2^U, U~U[-8,4]",
+                       "us": round(us, 2), "algorithmic_bytes": byts,
+                       "gbs": round(byts / (us * 1e-6) / 1e9, 2),
+                       "note": "input (64 MiB) stays in the 256 MB MALL "
+                               "across the two passes and back-to-back calls"}
+    del qi, qo
+
+    # large combine: 16384 tokens x 4096 from 147328 rows, top-8 of 128
+    cids, cw = si.large_combine_routing()
+    idsd = torch.from_numpy(cids).to(dev)
+    lay = mxq.moe_layout(idsd, 0, 128, "compact")
+    yl = si.gaussian_bf16_device(505, (lay["num_rows"], 4096), dev)
+    wd = torch.from_numpy(cw).to(dev)
+    ol = torch.empty((16384, 4096), dtype=torch.bfloat16, device=dev)
+    us = time_calls(torch, lambda: mxq.moe_combine(yl, lay["src2dst"], wd,
+                                                   out=ol))
+    byts = bytes_combine(16384, 8, 4096, 16384 * 8)
+    rows["large_combine"] = {"workload": "T=16384, hidden 4096, 128 experts "
+                                         "top-8, 147328-row layout",
+                             "us": round(us, 2), "algorithmic_bytes": byts,
+                             "gbs": round(byts / (us * 1e-6) / 1e9, 2)}
+    return rows
+
+
+# ------------------------------------------------------- CPU oracle leg
+
+def cpu_baseline(torch, si, b, y_dev, R, B_step, repeats):
+    """The CPU oracle, as it stands, on the same prefill workload: layout,
+    scatter+quant and combine over all 8192 tokens, median of `repeats`."""
+    import oracle
+    y_host = y_dev.view(torch.int16).cpu().numpy().view(np.uint16)
+    cores = oracle.max_threads()
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        lay = oracle.moe_layout(b.topk_ids, 0, b.n_local, "compact")
+        oracle.scatter_quant(b.x, lay["src2dst"], b.group, R)
+        oracle.combine(y_host, lay["src2dst"], b.topk_weights)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(B_step / t / 1e9, 3), "unit": "GB/s",
+            "cores": cores, "kind": "oracle",
+            "sample": "the full prefill workload (8192 tokens, 65536 "
+                      "assignments): layout + scatter_quant + combine, "
+                      "median of %d runs, %.2f s each" % (repeats, t),
+            "cpu_model": cpu_model}
+
+
+if __name__ == "__main__":
+    main()

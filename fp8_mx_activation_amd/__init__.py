@@ -129,6 +129,15 @@ def _u8(t: torch.Tensor) -> torch.Tensor:
     return t if t.dtype == torch.uint8 else t.view(torch.uint8)
 
 
+def _empty_rows_u8(rows: int, cols: int, device) -> torch.Tensor:
+    """[rows, cols] byte tensor whose rows start on 16-byte boundaries (the
+    library's vector-row requirement): a view of a padded allocation when
+    cols is not a multiple of 16."""
+    ld = -(-cols // 16) * 16
+    t = torch.empty((rows, ld), dtype=torch.uint8, device=device)
+    return t if ld == cols else t[:, :cols]
+
+
 # ---------------------------------------------------------------- host-only
 
 def moe_compact_row_bound(num_assignments: int, num_local_experts: int,
@@ -241,7 +250,7 @@ def moe_scatter_quant(x: torch.Tensor, src2dst: torch.Tensor, num_rows: int,
         raise ValueError("src2dst must be contiguous int32 [T, K]")
     K = src2dst.shape[1]
     if q is None:
-        q = torch.empty((num_rows, H), dtype=torch.uint8, device=x.device)
+        q = _empty_rows_u8(num_rows, H, x.device)
     if scales is None:
         scales = torch.empty((num_rows, H // G), dtype=torch.uint8,
                              device=x.device)
@@ -275,7 +284,7 @@ def mx_quant_live_rows(x: torch.Tensor, num_segments: int,
             num_segments or not live_counts.is_contiguous():
         raise ValueError("live_counts must be contiguous int32 [segments]")
     if q is None:
-        q = torch.empty((rows, H), dtype=torch.uint8, device=x.device)
+        q = _empty_rows_u8(rows, H, x.device)
     if scales is None:
         scales = torch.empty((rows, H // G), dtype=torch.uint8,
                              device=x.device)
@@ -322,7 +331,7 @@ def requant_per_token_to_per_tensor(q_in: torch.Tensor,
             not token_scales.is_contiguous():
         raise ValueError("token_scales must be contiguous float32 [T]")
     if q_out is None:
-        q_out = torch.empty((T, H), dtype=torch.uint8, device=qi.device)
+        q_out = _empty_rows_u8(T, H, qi.device)
     qo = _u8(q_out)
     ld_out = _rows(qo, "q_out", (torch.uint8,))
     if tensor_scale is None:

@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
             build()
         L = ctypes.CDLL(_LIB_PATH)
         sig = {
+            "ora_max_threads": (_i32, []),
+            "ora_set_threads": (None, [_i32]),
             "ora_e4m3_decode": (ctypes.c_double, [ctypes.c_uint8]),
             "ora_e4m3_encode": (ctypes.c_uint8, [ctypes.c_double]),
             "ora_bf16_round": (ctypes.c_uint16, [ctypes.c_float]),
@@ -94,6 +96,14 @@ def _ptr(a: np.ndarray) -> int:
 def _c(a, dtype) -> np.ndarray:
     a = np.ascontiguousarray(a, dtype=dtype)
     return a
+
+
+def max_threads() -> int:
+    return int(lib().ora_max_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().ora_set_threads(int(n))
 
 
 # ------------------------------------------------------------------ formats

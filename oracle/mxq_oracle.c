@@ -47,11 +47,16 @@
  * error bounds.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORA_E4M3_MAX 448.0
+
+/* Thread control for timing runs (no arithmetic). */
+int32_t ora_max_threads(void) { return omp_get_max_threads(); }
+void ora_set_threads(int32_t n) { omp_set_num_threads(n); }
 
 /* ---------------------------------------------------------------- formats */
 
