@@ -107,6 +107,27 @@ def time_calls(torch, fn, reps=20, warmup=3):
     return float(np.median(per)) * 1e3  # microseconds
 
 
+def graph_step_ms(torch, fn, warmup, steps):
+    """Capture fn once in a hipGraph; time `steps` replays."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def traffic_record():
     """HBM bytes per combine launch from committed rocprofv3 counters, or
     None if absent or taken on another version of the kernel source."""
@@ -213,6 +234,11 @@ def main():
     step_ms = wall_s * 1e3 / args.steps
     ev_step_ms = float(np.mean(lay_ms) + np.mean(sq_ms) + np.mean(cb_ms))
 
+    # the same step captured once in a hipGraph and replayed (no per-kernel
+    # host launch cost); reported beside the eager timed region
+    graph_ms = graph_step_ms(torch, lambda: step(False), args.warmup,
+                             args.steps)
+
     value = B_step / (step_ms * 1e-3) / 1e9
     cb_gbs = B_cb / (np.mean(cb_ms) * 1e-3) / 1e9
     sq_gbs = B_sq / (np.mean(sq_ms) * 1e-3) / 1e9
@@ -243,6 +269,8 @@ def main():
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "assignments_per_s": round(A / (step_ms * 1e-3), 1),
+        "graph_replay": {"ms_per_step": round(graph_ms, 4),
+                         "gbs": round(B_step / (graph_ms * 1e-3) / 1e9, 2)},
         "scatter_quant_plus_combine": {
             "bytes": B_sq + B_cb,
             "us": round(1e3 * (np.mean(sq_ms) + np.mean(cb_ms)), 2),

@@ -11,7 +11,8 @@
 // One block per token; a lane owns 8 consecutive channels.  The K rows of a
 // token are loaded as independent 16-byte vectors before any arithmetic, so
 // each lane has up to eight loads in flight.  Per token the kernel reads
-// K valid rows of 2H bytes and writes one row.
+// K valid rows of 2H bytes and writes one row; the output row is written
+// with streaming (non-temporal) stores so it does not displace cached lines.
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
 
@@ -64,14 +65,14 @@ __global__ __launch_bounds__(1024) void combine_kernel(
     }
     if constexpr (F32_OUT) {
       float* o = static_cast<float*>(out) + t * ld_out + col;
-      store16(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                       __float_as_uint(acc[2]), __float_as_uint(acc[3])});
-      store16(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
-                           __float_as_uint(acc[6]), __float_as_uint(acc[7])});
+      store16_nt(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                          __float_as_uint(acc[2]), __float_as_uint(acc[3])});
+      store16_nt(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                              __float_as_uint(acc[6]), __float_as_uint(acc[7])});
     } else {
       uint16_t* o = static_cast<uint16_t*>(out) + t * ld_out + col;
-      store16(o, u32x4{bf16x2_rne(acc[0], acc[1]), bf16x2_rne(acc[2], acc[3]),
-                       bf16x2_rne(acc[4], acc[5]), bf16x2_rne(acc[6], acc[7])});
+      store16_nt(o, u32x4{bf16x2_rne(acc[0], acc[1]), bf16x2_rne(acc[2], acc[3]),
+                          bf16x2_rne(acc[4], acc[5]), bf16x2_rne(acc[6], acc[7])});
     }
   }
 }

@@ -7,25 +7,37 @@
 // slots with masked_m, overflow fails fast).  Slots inside an expert follow
 // ascending flat assignment index t*K + j.
 //
-// Two launches with grids fixed by T*K:
-//   layout_hist_kernel    one block per chunk: LDS histogram of the chunk's
-//                         local experts -> ws[chunk][E].
-//   layout_assign_kernel  four chunks per block (one per wavefront):
-//     A  every block sums ws over all chunks (totals c_e) and over the
-//        chunks before each of its wavefronts (first slot per expert);
-//     B  wavefront 0 scans the padded region sizes into region starts;
-//     C  each wavefront walks its chunk 64 assignments at a time.  Lanes with
-//        the same expert are found with one ballot per key bit (a bit-sliced
-//        multi-split); a lane's rank among them is the popcount of matching
-//        lower lanes, so slots are assigned in flat order without atomics;
-//     D  all blocks fill m_indices over [0, num_rows) with a grid-stride loop;
-//     E  block 0 publishes counts, region starts, masked_m and the flag.
+// Three launches whose grids depend only on T*K, E and num_rows:
+//   layout_hist_kernel    one block per chunk of assignments: LDS histogram
+//                         of the chunk's local experts -> cnt[chunk][E].
+//   layout_scan_kernel    one block, one thread per expert: turns the chunk
+//                         counts into each chunk's first slot (in place),
+//                         the totals c_e and, by a block-wide scan of the
+//                         padded sizes, the region starts; publishes counts,
+//                         region starts, masked_m and the overflow flag.
+//   layout_assign_kernel  one block of 16 wavefronts per chunk, plus enough
+//                         blocks for the m_indices fill:
+//     C  each wavefront ranks its own steps of 64 assignments: lanes with the
+//        same expert are found with one ballot per key bit (a bit-sliced
+//        multi-split) and a lane's rank among them is the popcount of the
+//        matching lower lanes.  Per-wavefront expert counts are then
+//        prefix-summed across the block, so slots follow flat order without
+//        atomics and without a serial walk over the chunk.
+//     D  rows are mapped to experts through an LDS table with one entry per
+//        block_e rows (regions start on multiples of block_e), or a binary
+//        search over the region starts when that table would not fit in the
+//        LDS left over (64 KB per block in all).
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
 
 namespace {
 
 using namespace mxq;
+
+constexpr int kScanBatch = 64;
+constexpr int kAssignWaves = 16;
+constexpr int kMaxStepsPerWave = kChunkMax / (64 * kAssignWaves);
+constexpr int kAssignLds = 65536;  // LDS bytes of the assign kernel
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi(
@@ -34,7 +46,7 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 
 __global__ __launch_bounds__(256) void layout_hist_kernel(
     const int32_t* __restrict__ ids, int64_t A, int32_t begin, int32_t E,
-    int32_t chunk, int32_t* __restrict__ ws) {
+    int32_t chunk, int32_t* __restrict__ cnt) {
   extern __shared__ int32_t hist[];
   for (int i = threadIdx.x; i < E; i += 256) hist[i] = 0;
   __syncthreads();
@@ -46,141 +58,231 @@ __global__ __launch_bounds__(256) void layout_hist_kernel(
   }
   __syncthreads();
   for (int i = threadIdx.x; i < E; i += 256)
-    ws[(int64_t)blockIdx.x * E + i] = hist[i];
+    cnt[(int64_t)blockIdx.x * E + i] = hist[i];
 }
 
-__global__ __launch_bounds__(256) void layout_assign_kernel(
+// Workspace after this kernel: base[c][e] (first slot of chunk c in expert
+// e, overwriting the counts), tot[e], off[e] (E + 1 entries).
+__global__ __launch_bounds__(1024) void layout_scan_kernel(
+    int32_t* __restrict__ base, int32_t* __restrict__ tot_ws,
+    int32_t* __restrict__ off_ws, int32_t E, int32_t nc, int32_t kind,
+    int32_t block_e, int32_t cap, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ masked_m,
+    int32_t* __restrict__ overflow) {
+  __shared__ int32_t wsum[16];
+  const int e = threadIdx.x;
+  const int lane = e & 63;
+  const int wv = e >> 6;
+  int total = 0;
+  if (e < E) {
+    for (int c0 = 0; c0 < nc; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)  // a batch of loads in flight
+        v[i] = base[(int64_t)min(c0 + i, nc - 1) * E + e];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (c0 + i < nc) {
+          base[(int64_t)(c0 + i) * E + e] = total;
+          total += v[i];
+        }
+      }
+    }
+  }
+  int padded = 0;
+  if (e < E) {
+    if (kind == 0) {
+      padded = (total + block_e - 1) / block_e * block_e;
+    } else {
+      padded = cap;
+    }
+  }
+  // block-wide exclusive scan of the padded sizes (E <= 1024)
+  int incl = padded;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  const int nwaves = blockDim.x >> 6;
+  for (int w = 0; w < nwaves; ++w) before += (w < wv) ? wsum[w] : 0;
+  const int start = before + incl - padded;
+  int grand = 0;
+  for (int w = 0; w < nwaves; ++w) grand += wsum[w];
+  if (e < E) {
+    tot_ws[e] = total;
+    off_ws[e] = start;
+    counts[e] = total;
+    offsets[e] = start;
+    if (masked_m != nullptr) masked_m[e] = kind == 1 ? min(total, cap) : total;
+  }
+  if (e == 0) {
+    off_ws[E] = grand;
+    offsets[E] = grand;
+  }
+  const int ovf = (e < E && kind == 1 && total > cap) ? 1 : 0;
+  const int any = __syncthreads_or(ovf);
+  if (e == 0) *overflow = any ? 1 : 0;
+}
+
+// Slots: one block of kAssignWaves wavefronts per chunk.  Each wavefront
+// owns a contiguous run of whole 64-assignment steps; it ranks its lanes
+// within each step (ballot multi-split) and among its own earlier steps, and
+// publishes its per-expert counts to LDS.  After a barrier the counts are
+// prefix-summed over the wavefronts, so a lane's slot is
+// chunk base + count of the same expert in earlier wavefronts + its rank in
+// its wavefront: flat order, no atomics, no serial chain across wavefronts.
+__global__ __launch_bounds__(1024) void layout_assign_kernel(
     const int32_t* __restrict__ ids, int64_t A, int32_t begin, int32_t E,
     int32_t nbits, int32_t kind, int32_t block_e, int32_t cap,
-    int64_t num_rows, int32_t chunk, int32_t nc,
-    const int32_t* __restrict__ ws, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ m_indices,
-    int32_t* __restrict__ masked_m, int32_t* __restrict__ src2dst,
-    int32_t* __restrict__ overflow) {
+    int64_t num_rows, int32_t chunk, int32_t nc, int32_t steps_per_wave,
+    int32_t tbl_cap, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ tot_ws, const int32_t* __restrict__ off_ws,
+    int32_t* __restrict__ m_indices, int32_t* __restrict__ src2dst) {
   extern __shared__ int32_t sm[];
-  int32_t* tot = sm;               // [E]
-  int32_t* off = sm + E;           // [E + 1]
-  int32_t* run = sm + 2 * E + 1;   // [4][E] next free slot per wavefront
+  int32_t* tot = sm;                   // [E]
+  int32_t* off = sm + E;               // [E + 1]
+  int32_t* cbase = sm + 2 * E + 1;     // [E] first slot of this chunk
+  int32_t* tbl = sm + 3 * E + 1;       // [tbl_cap] expert per block_e rows
+  // [kAssignWaves][E] per-wavefront counts, then their prefixes (< chunk)
+  uint16_t* cnt = reinterpret_cast<uint16_t*>(tbl + tbl_cap);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int c0 = blockIdx.x * 4;
+  const int c = blockIdx.x;
+  const bool has_chunk = c < nc;
+  const int64_t c_begin = (int64_t)c * chunk;
+  const int64_t c_end = has_chunk ? min(c_begin + (int64_t)chunk, A) : c_begin;
+  const int64_t w_begin = c_begin + (int64_t)wv * steps_per_wave * 64;
+  const int64_t w_end = min(w_begin + (int64_t)steps_per_wave * 64, c_end);
 
-  // A: totals and first slots
-  for (int e = tid; e < E; e += 256) {
-    int all = 0, pre = 0, l0 = 0, l1 = 0, l2 = 0;
-#pragma unroll 8
-    for (int c = 0; c < nc; ++c) {
-      const int v = ws[(int64_t)c * E + e];
-      all += v;
-      pre += (c < c0) ? v : 0;
-      l0 += (c == c0) ? v : 0;
-      l1 += (c == c0 + 1) ? v : 0;
-      l2 += (c == c0 + 2) ? v : 0;
-    }
-    tot[e] = all;
-    run[e] = pre;
-    run[E + e] = pre + l0;
-    run[2 * E + e] = pre + l0 + l1;
-    run[3 * E + e] = pre + l0 + l1 + l2;
+  // this wavefront's ids, fetched before anything waits
+  int32_t idb[kMaxStepsPerWave];
+#pragma unroll
+  for (int st = 0; st < kMaxStepsPerWave; ++st) {
+    const int64_t a = w_begin + st * 64 + lane;
+    idb[st] = (st < steps_per_wave && a < w_end) ? ids[a] : 0;
   }
+  for (int i = tid; i < E; i += blockDim.x) {
+    tot[i] = tot_ws[i];
+    off[i] = off_ws[i];
+    cbase[i] = has_chunk ? base[(int64_t)c * E + i] : 0;
+  }
+  if (tid == 0) off[E] = off_ws[E];
+  for (int i = tid; i < kAssignWaves * E; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
 
-  // B: region starts
-  if (wv == 0) {
-    const int per = (E + 63) / 64;
-    const int lo = lane * per;
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = lo + i;
-      if (e < E) sum += kind == 0 ? (tot[e] + block_e - 1) / block_e * block_e : cap;
-    }
-    int incl = sum;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    int start = incl - sum;
-    for (int i = 0; i < per; ++i) {
-      const int e = lo + i;
-      if (e < E) {
-        off[e] = start;
-        start += kind == 0 ? (tot[e] + block_e - 1) / block_e * block_e : cap;
-      }
-    }
-    if (lane == 63) off[E] = incl;
-  }
-  __syncthreads();
-
-  // C: stable slots, one wavefront per chunk
-  const int c = c0 + wv;
-  if (c < nc) {
-    int32_t* runw = run + wv * E;
-    const int64_t a_begin = (int64_t)c * chunk;
-    const int64_t a_end = min(a_begin + (int64_t)chunk, A);
-    for (int64_t a0 = a_begin; a0 < a_end; a0 += 64) {
-      const int64_t a = a0 + lane;
-      const bool valid = a < a_end;
-      const int64_t e64 = valid ? (int64_t)ids[a] - begin : -1;
+  // C1: ranks inside the wavefront
+  int key[kMaxStepsPerWave];
+  int rank[kMaxStepsPerWave];
+  if (has_chunk) {
+    uint16_t* cw = cnt + wv * E;
+#pragma unroll
+    for (int st = 0; st < kMaxStepsPerWave; ++st) {
+      key[st] = -1;
+      rank[st] = 0;
+      if (st >= steps_per_wave || w_begin + st * 64 >= w_end) continue;
+      const int64_t a = w_begin + st * 64 + lane;
+      const int64_t e64 = a < w_end ? (int64_t)idb[st] - begin : -1;
       const bool local = e64 >= 0 && e64 < E;
-      const int e = local ? (int)e64 : 0;
-      uint64_t match = __ballot(local);
+      const int ke = local ? (int)e64 : 0;
+      uint64_t m = __ballot(local);
       for (int bit = 0; bit < nbits; ++bit) {
-        const bool set = (e >> bit) & 1;
+        const bool set = (ke >> bit) & 1;
         const uint64_t bb = __ballot(local && set);
-        match &= set ? bb : ~bb;
+        m &= set ? bb : ~bb;
       }
-      const int rank = lanes_below(match);
-      int slot = 0;
-      if (local) slot = runw[e] + rank;
-      // All lanes of the wavefront have read runw[e] (same instruction)
-      // before the lowest matching lane advances it.
-      if (local && rank == 0) runw[e] = slot + (int)__popcll(match);
+      const int r = lanes_below(m);
+      int prev = 0;
+      if (local) prev = cw[ke];
+      // every lane has read cw[ke] (same instruction) before the lowest lane
+      // of each expert advances it
+      if (local && r == 0) cw[ke] = (uint16_t)(prev + (int)__popcll(m));
+      key[st] = local ? ke : -1;
+      rank[st] = prev + r;
+    }
+  }
+  __syncthreads();
+  // C2: exclusive prefix of the per-wavefront counts (within the chunk)
+  if (has_chunk) {
+    for (int e = tid; e < E; e += blockDim.x) {
+      int run = 0;
+#pragma unroll
+      for (int w = 0; w < kAssignWaves; ++w) {
+        const int v = cnt[w * E + e];
+        cnt[w * E + e] = (uint16_t)run;
+        run += v;
+      }
+    }
+  }
+  __syncthreads();
+  // C3: destinations
+  if (has_chunk) {
+#pragma unroll
+    for (int st = 0; st < kMaxStepsPerWave; ++st) {
+      if (st >= steps_per_wave) break;
+      const int64_t a = w_begin + st * 64 + lane;
+      if (a >= w_end) break;
+      const int e = key[st];
       int32_t dst = -1;
-      if (local) {
+      if (e >= 0) {
+        const int slot = cbase[e] + (int)cnt[wv * E + e] + rank[st];
         if (kind == 0)
           dst = off[e] + slot;
         else
           dst = slot < cap ? e * cap + slot : -1;
       }
-      if (valid) src2dst[a] = dst;
+      src2dst[a] = dst;
     }
   }
 
   // D: m_indices
-  if (m_indices != nullptr) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t r = (int64_t)blockIdx.x * 256 + tid; r < num_rows; r += stride) {
+  if (m_indices == nullptr) return;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t r_first = (int64_t)blockIdx.x * blockDim.x + tid;
+  if (kind == 1) {
+    for (int64_t r = r_first; r < num_rows; r += stride) {
+      const int64_t e = r / cap;
       int32_t v = -1;
-      if (kind == 0) {
-        if (r < off[E]) {
-          int lo = 0, hi = E - 1;  // largest e with off[e] <= r
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (off[mid] <= r) lo = mid; else hi = mid - 1;
-          }
-          if (r - off[lo] < tot[lo]) v = lo;
-        }
-      } else {
-        const int64_t e = r / cap;
-        if (e < E && r - e * cap < min(tot[e], cap)) v = (int32_t)e;
-      }
+      if (e < E && r - e * cap < min(tot[e], cap)) v = (int32_t)e;
       m_indices[r] = v;
     }
+    return;
   }
-
-  // E: per-expert outputs and the overflow flag
-  if (blockIdx.x == 0) {
-    int ovf = 0;
-    for (int e = tid; e < E; e += 256) {
-      counts[e] = tot[e];
-      offsets[e] = off[e];
-      if (masked_m != nullptr) masked_m[e] = kind == 1 ? min(tot[e], cap) : tot[e];
-      ovf |= (kind == 1 && tot[e] > cap) ? 1 : 0;
+  const int32_t used = off[E];
+  const int32_t nblk = (used + block_e - 1) / block_e;
+  const bool use_tbl = nblk <= tbl_cap;
+  if (use_tbl) {
+    for (int i = tid; i < nblk; i += blockDim.x) {
+      const int32_t r = i * block_e;
+      int lo = 0, hi = E - 1;  // largest e with off[e] <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      tbl[i] = lo;
     }
-    if (tid == 0) offsets[E] = off[E];
-    const int any = __syncthreads_or(ovf);
-    if (tid == 0) *overflow = any ? 1 : 0;
+  }
+  __syncthreads();
+  for (int64_t r = r_first; r < num_rows; r += stride) {
+    int32_t v = -1;
+    if (r < used) {
+      int e;
+      if (use_tbl) {
+        e = tbl[(int32_t)r / block_e];
+      } else {
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (off[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        e = lo;
+      }
+      if (r - off[e] < tot[e]) v = e;
+    }
+    m_indices[r] = v;
   }
 }
 
@@ -198,8 +300,8 @@ extern "C" mxq_status moe_layout(
       E > MXQ_MAX_LOCAL_EXPERTS)
     return MXQ_ERR_INVALID_ARGUMENT;
   const int64_t A = T * (int64_t)K;
-  if (A > INT32_MAX || num_rows < 0 || num_rows > INT32_MAX)
-    return MXQ_ERR_INVALID_ARGUMENT;
+  if (num_rows < 0 || num_rows > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
+  if (A > MXQ_MAX_ASSIGNMENTS) return MXQ_ERR_UNSUPPORTED;
   if (kind == MXQ_LAYOUT_COMPACT) {
     if (block_e < 1) return MXQ_ERR_INVALID_ARGUMENT;
     if (num_rows < moe_compact_row_bound(A, E, block_e))
@@ -216,23 +318,42 @@ extern "C" mxq_status moe_layout(
     return MXQ_ERR_INVALID_ARGUMENT;
   const LayoutGeom g = layout_geom(A);
   const size_t need = layout_workspace_bytes(A, E);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return MXQ_ERR_WORKSPACE;
+  if (workspace == nullptr || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
 
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   hipStream_t s = as_stream(stream);
-  int32_t* ws = static_cast<int32_t*>(workspace);
+  int32_t* base = static_cast<int32_t*>(workspace);
+  int32_t* tot_ws = base + (size_t)g.nc * E;
+  int32_t* off_ws = tot_ws + E;
+  const int32_t cap = kind == MXQ_LAYOUT_MASKED ? capacity : 0;
   if (g.nc > 0) {
     layout_hist_kernel<<<g.nc, 256, (size_t)E * sizeof(int32_t), s>>>(
-        topk_ids, A, expert_begin, E, g.chunk, ws);
+        topk_ids, A, expert_begin, E, g.chunk, base);
     if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;
   }
-  const int blocks = g.nc > 0 ? (int)ceil_div(g.nc, 4) : 1;
-  const size_t lds = (size_t)(6 * E + 1) * sizeof(int32_t);
-  layout_assign_kernel<<<blocks, 256, lds, s>>>(
-      topk_ids, A, expert_begin, E, nbits, (int32_t)kind, block_e,
-      kind == MXQ_LAYOUT_MASKED ? capacity : 0, num_rows, g.chunk, g.nc, ws,
-      counts, expert_offsets, m_indices, masked_m, src2dst, overflow_flag);
+  const int scan_threads = (int)ceil_div(E, 64) * 64;
+  layout_scan_kernel<<<1, scan_threads, 0, s>>>(
+      base, tot_ws, off_ws, E, g.nc, (int32_t)kind, block_e, cap, counts,
+      expert_offsets, masked_m, overflow_flag);
+  if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;
+  // One block per chunk; more blocks (up to 64) if the m_indices fill needs
+  // them.  Each of the 16 wavefronts of a block takes steps_per_wave steps.
+  const int32_t steps_per_wave =
+      (int32_t)ceil_div(ceil_div(g.chunk, 64), kAssignWaves);
+  int64_t blocks = g.nc;
+  if (m_indices != nullptr) {
+    int64_t fill_blocks = ceil_div(num_rows, 4096);
+    if (fill_blocks > 64) fill_blocks = 64;
+    if (fill_blocks > blocks) blocks = fill_blocks;
+  }
+  if (blocks == 0) return MXQ_OK;
+  const size_t fixed = (size_t)(3 * E + 1) * sizeof(int32_t) +
+                       (size_t)kAssignWaves * E * sizeof(uint16_t);
+  const int32_t tbl_cap = (int32_t)((kAssignLds - fixed) / sizeof(int32_t));
+  layout_assign_kernel<<<(unsigned)blocks, 1024, kAssignLds, s>>>(
+      topk_ids, A, expert_begin, E, nbits, (int32_t)kind, block_e, cap,
+      num_rows, g.chunk, g.nc, steps_per_wave, tbl_cap, base, tot_ws, off_ws,
+      m_indices, src2dst);
   return launch_status();
 }

@@ -46,10 +46,13 @@ inline int row_block_threads(int64_t H, int per_lane) {
 
 namespace mxq {
 
-// Layout work split: the T*K assignments are cut into at most kLayoutChunks
-// chunks of a whole number of 64-assignment steps; one wavefront owns a
-// chunk.  The split depends only on T*K, so the grid is static.
-constexpr int kLayoutChunks = 64;
+// Layout work split: the T*K assignments are cut into chunks of a whole
+// number of 1024-assignment groups (at least 1024, at most 8192, aiming at
+// 64 chunks); one block of 16 wavefronts owns a chunk.  The split depends
+// only on T*K, so the grid is static.
+constexpr int kChunkMin = 1024;
+constexpr int kChunkMax = 8192;
+constexpr int kChunksTarget = 64;
 
 struct LayoutGeom {
   int32_t nc;     // number of chunks (0 when there are no assignments)
@@ -57,19 +60,21 @@ struct LayoutGeom {
 };
 
 inline LayoutGeom layout_geom(int64_t A) {
-  LayoutGeom g{0, 64};
+  LayoutGeom g{0, kChunkMin};
   if (A <= 0) return g;
-  int64_t nc = ceil_div(A, 64);
-  if (nc > kLayoutChunks) nc = kLayoutChunks;
-  int64_t chunk = ceil_div(ceil_div(A, nc), 64) * 64;
+  int64_t chunk = ceil_div(ceil_div(A, kChunksTarget), kChunkMin) * kChunkMin;
+  if (chunk > kChunkMax) chunk = kChunkMax;
   g.chunk = (int32_t)chunk;
   g.nc = (int32_t)ceil_div(A, chunk);
   return g;
 }
 
+// Workspace: per-chunk counts (then first slots) [nc][E], totals [E] and
+// region starts [E + 1].
 inline size_t layout_workspace_bytes(int64_t A, int32_t E) {
   LayoutGeom g = layout_geom(A);
-  return (size_t)g.nc * (size_t)(E > 0 ? E : 0) * sizeof(int32_t);
+  const size_t e = (size_t)(E > 0 ? E : 0);
+  return ((size_t)g.nc * e + 2 * e + 1) * sizeof(int32_t);
 }
 
 }  // namespace mxq

@@ -7,10 +7,9 @@
 //
 // Work split: one block per token row (scatter) or per live row (send side);
 // a lane owns 16 consecutive channels, so one row is read once with 16-byte
-// loads, its group exponents come from in-wavefront max reductions, and the
-// 16 fp8 bytes a lane produces go to every destination row with one 16-byte
-// store each.  The scatter path is bandwidth-bound: per token it reads 2H
-// bytes and writes K*(H + H/G) bytes.
+// loads and its group exponents come from in-wavefront max reductions.  The
+// scatter path is bandwidth-bound: per token it reads 2H bytes and writes
+// K*(H + H/G) bytes.
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
 
@@ -18,14 +17,23 @@ namespace {
 
 using namespace mxq;
 
-// One block per token.  Destinations come from src2dst (uniform per block,
-// so they are scalar loads); a token without a destination in [0, num_rows)
-// is skipped before its row is read.
+// One block per token, in two phases.  Phase 1: the block reads the token
+// row once (16-byte loads, a lane owns 16 channels), quantizes it and stages
+// the fp8 row and its scale bytes in LDS.  Phase 2: wavefront w writes
+// destinations j = w, w + nw, ...; each destination row is written by one
+// wavefront as a contiguous run of 1 KB streaming (non-temporal) stores,
+// followed by its scale bytes.  Writing whole rows per wavefront and
+// bypassing cache allocation for the write-once payload keeps the HBM write
+// stream sequential; the scale bytes use ordinary stores so partial lines
+// merge in L2.  Destinations come from src2dst (uniform per block: scalar
+// loads); a token without a destination in [0, num_rows) is skipped before
+// its row is read.
 template <int G>
 __global__ __launch_bounds__(1024) void scatter_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, int32_t H,
     const int32_t* __restrict__ src2dst, int32_t K, uint8_t* __restrict__ q,
     int64_t ld_q, uint8_t* __restrict__ s, int64_t ld_s, int64_t num_rows) {
+  extern __shared__ __align__(16) uint8_t row[];  // [H] fp8, then [H/G] scales
   const int64_t t = blockIdx.x;
   const int32_t* dl = src2dst + t * K;
   bool any = false;
@@ -41,13 +49,21 @@ __global__ __launch_bounds__(1024) void scatter_quant_kernel(
     const u32x4 b = load16(xr + col + 8);
     int e;
     const u32x4 v = quant16<G>(a, b, e);
-    const uint8_t sb = (uint8_t)(e + 127);
-    for (int j = 0; j < K; ++j) {
-      const int64_t d = dl[j];
-      if (d < 0 || d >= num_rows) continue;
-      store16(q + d * ld_q + col, v);
-      if (lead) s[d * ld_s + col / G] = sb;
-    }
+    *reinterpret_cast<u32x4*>(row + col) = v;
+    if (lead) row[H + col / G] = (uint8_t)(e + 127);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  const int ng = H / G;
+  for (int j = threadIdx.x >> 6; j < K; j += nw) {
+    const int64_t d = dl[j];
+    if (d < 0 || d >= num_rows) continue;
+    uint8_t* qr = q + d * ld_q;
+    for (int c = lane * 16; c < H; c += 64 * 16)
+      store16_nt(qr + c, *reinterpret_cast<const u32x4*>(row + c));
+    uint8_t* sr = s + d * ld_s;
+    for (int g = lane; g < ng; g += 64) sr[g] = row[H + g];
   }
 }
 
@@ -117,6 +133,7 @@ extern "C" mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x,
   if (T < 0 || T > INT32_MAX || H <= 0 || H % G != 0 || K < 0 ||
       K > MXQ_MAX_TOPK || num_rows < 0 || num_rows > INT32_MAX)
     return MXQ_ERR_INVALID_ARGUMENT;
+  if (H > MXQ_MAX_HIDDEN) return MXQ_ERR_UNSUPPORTED;
   if (T == 0 || K == 0) return MXQ_OK;
   if (x_bf16 == nullptr || src2dst == nullptr || ld_x < H)
     return MXQ_ERR_INVALID_ARGUMENT;
@@ -127,15 +144,18 @@ extern "C" mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x,
     return MXQ_ERR_INVALID_ARGUMENT;
   if (num_rows == 0) return MXQ_OK;
 
-  const int threads = row_block_threads(H, 16);
+  // 1024 threads: at most two tokens in flight per CU, which keeps the
+  // number of concurrent destination-row write streams low.
+  const int threads = 1024;
+  const size_t lds = (size_t)H + (size_t)(H / G);
   hipStream_t s = as_stream(stream);
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   uint8_t* q = static_cast<uint8_t*>(q_fp8);
   if (G == 128)
-    scatter_quant_kernel<128><<<(unsigned)T, threads, 0, s>>>(
+    scatter_quant_kernel<128><<<(unsigned)T, threads, lds, s>>>(
         x, ld_x, H, src2dst, K, q, ld_q, scales, ld_s, num_rows);
   else
-    scatter_quant_kernel<32><<<(unsigned)T, threads, 0, s>>>(
+    scatter_quant_kernel<32><<<(unsigned)T, threads, lds, s>>>(
         x, ld_x, H, src2dst, K, q, ld_q, scales, ld_s, num_rows);
   return launch_status();
 }

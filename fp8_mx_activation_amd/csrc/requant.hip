@@ -4,16 +4,18 @@
 // breakdown items 1-2).
 //
 // Two launches with static grids:
-//   requant_amax_kernel   kPartials blocks; a wavefront takes whole rows, gets
-//                         the row's largest magnitude byte with packed 16-bit
-//                         max operations and a wavefront max, decodes it and
-//                         multiplies by the token scale; each block writes the
-//                         max of its rows (fp32 bits of a non-negative float
-//                         order like unsigned integers) to workspace.
+//   requant_amax_kernel   up to kPartials blocks; a wavefront takes four whole
+//                         rows at a time, gets each row's largest magnitude
+//                         byte with packed 16-bit max operations and a
+//                         wavefront max, decodes it and multiplies by the
+//                         token scale; each block writes the max of its rows
+//                         (fp32 bits of a non-negative float order like
+//                         unsigned integers) to workspace.
 //   requant_apply_kernel  every block reduces the partials (a few KB from
 //                         L2), forms S = amax / 448 and 1 / S with IEEE
-//                         division, then rewrites its rows:
-//                         q' = e4m3((dec(q) * s_t) * (1 / S)).
+//                         division, then rewrites its rows four at a time:
+//                         q' = e4m3((dec(q) * s_t) * (1 / S)), written with
+//                         streaming stores.
 // The input is read twice; at 16384 x 4096 it is 64 MiB, which the 256 MB
 // last-level cache of MI355X holds between the two passes.
 #include "mxq_device.hpp"
@@ -23,7 +25,7 @@ namespace {
 
 using namespace mxq;
 
-constexpr int kPartials = 512;
+constexpr int kPartials = 1024;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -47,24 +49,42 @@ __device__ __forceinline__ uint32_t requant4(uint32_t w, float st, float inv) {
                     (hi[0] * st) * inv, (hi[1] * st) * inv);
 }
 
+// A wavefront owns rows w, w + S, w + 2S, w + 3S (S = number of
+// wavefronts) at a time, so each lane keeps up to 16 loads in flight.
+constexpr int kRowsPerWave = 4;
+
 __global__ __launch_bounds__(256) void requant_amax_kernel(
     const uint8_t* __restrict__ q, int64_t ld, const float* __restrict__ sc,
     int64_t T, int32_t H, uint32_t* __restrict__ partial) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int64_t H16 = (int64_t)(H / 16) * 16;
+  const int64_t S = (int64_t)gridDim.x * 4;
   uint32_t best = 0;
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wv; row < T;
-       row += (int64_t)gridDim.x * 4) {
-    const uint8_t* r = q + row * ld;
-    uint32_t m = 0;
-    for (int64_t col = lane * 16; col < H16; col += 64 * 16)
-      m = max(m, mag_max16(load16(r + col)));
-    for (int64_t col = H16 + lane; col < H; col += 64)
-      m = max(m, (uint32_t)(r[col] & 0x7F));
-    m = wave_max(m);
-    const float rq = __builtin_amdgcn_cvt_f32_fp8((int)m, 0) * sc[row];
-    best = max(best, __float_as_uint(rq));
+  for (int64_t r0 = (int64_t)blockIdx.x * 4 + wv; r0 < T; r0 += S * kRowsPerWave) {
+    uint32_t m[kRowsPerWave] = {0, 0, 0, 0};
+#pragma unroll 4
+    for (int64_t col = lane * 16; col < H16; col += 64 * 16) {
+      u32x4 v[kRowsPerWave];
+#pragma unroll
+      for (int u = 0; u < kRowsPerWave; ++u) {
+        const int64_t row = r0 + u * S;
+        v[u] = row < T ? load16(q + row * ld + col) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < kRowsPerWave; ++u) m[u] = max(m[u], mag_max16(v[u]));
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsPerWave; ++u) {
+      const int64_t row = r0 + u * S;
+      if (row >= T) break;
+      const uint8_t* r = q + row * ld;
+      for (int64_t col = H16 + lane; col < H; col += 64)
+        m[u] = max(m[u], (uint32_t)(r[col] & 0x7F));
+      const uint32_t mm = wave_max(m[u]);
+      const float rq = __builtin_amdgcn_cvt_f32_fp8((int)mm, 0) * sc[row];
+      best = max(best, __float_as_uint(rq));
+    }
   }
   __shared__ uint32_t red[4];
   best = wave_max(best);
@@ -90,27 +110,47 @@ __global__ __launch_bounds__(256) void requant_apply_kernel(
   if (lane == 0) red[wv] = m;
   __syncthreads();
   const float amax = __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])));
-  const float S = amax > 0.0f ? amax / 448.0f : 1.0f;
-  const float inv = 1.0f / S;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = S;
+  const float S_t = amax > 0.0f ? amax / 448.0f : 1.0f;
+  const float inv = 1.0f / S_t;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = S_t;
 
   const int64_t H16 = (int64_t)(H / 16) * 16;
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wv; row < T;
-       row += (int64_t)gridDim.x * 4) {
-    const float st = sc[row];
-    const uint8_t* ri = q_in + row * ld_in;
-    uint8_t* ro = q_out + row * ld_out;
-    for (int64_t col = lane * 16; col < H16; col += 64 * 16) {
-      const u32x4 v = load16(ri + col);
-      u32x4 o;
-      o.x = requant4(v.x, st, inv);
-      o.y = requant4(v.y, st, inv);
-      o.z = requant4(v.z, st, inv);
-      o.w = requant4(v.w, st, inv);
-      store16(ro + col, o);
+  const int64_t S = (int64_t)gridDim.x * 4;
+  for (int64_t r0 = (int64_t)blockIdx.x * 4 + wv; r0 < T; r0 += S * kRowsPerWave) {
+    float st[kRowsPerWave];
+#pragma unroll
+    for (int u = 0; u < kRowsPerWave; ++u) {
+      const int64_t row = r0 + u * S;
+      st[u] = row < T ? sc[row] : 0.0f;
     }
-    for (int64_t col = H16 + lane; col < H; col += 64)
-      ro[col] = (uint8_t)requant4(ri[col], st, inv);
+#pragma unroll 2
+    for (int64_t col = lane * 16; col < H16; col += 64 * 16) {
+      u32x4 v[kRowsPerWave];
+#pragma unroll
+      for (int u = 0; u < kRowsPerWave; ++u) {
+        const int64_t row = r0 + u * S;
+        v[u] = row < T ? load16(q_in + row * ld_in + col) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < kRowsPerWave; ++u) {
+        const int64_t row = r0 + u * S;
+        if (row >= T) break;
+        u32x4 o;
+        o.x = requant4(v[u].x, st[u], inv);
+        o.y = requant4(v[u].y, st[u], inv);
+        o.z = requant4(v[u].z, st[u], inv);
+        o.w = requant4(v[u].w, st[u], inv);
+        store16_nt(q_out + row * ld_out + col, o);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsPerWave; ++u) {
+      const int64_t row = r0 + u * S;
+      if (row >= T) break;
+      for (int64_t col = H16 + lane; col < H; col += 64)
+        q_out[row * ld_out + col] =
+            (uint8_t)requant4(q_in[row * ld_in + col], st[u], inv);
+    }
   }
 }
 
@@ -143,7 +183,7 @@ extern "C" mxq_status requant_per_token_to_per_tensor(
 
   hipStream_t s = as_stream(stream);
   uint32_t* partial = static_cast<uint32_t*>(workspace);
-  int64_t np = ceil_div(T, 4);
+  int64_t np = ceil_div(T, 4 * kRowsPerWave);
   if (np > kPartials) np = kPartials;
   if (np > 0) {
     requant_amax_kernel<<<(unsigned)np, 256, 0, s>>>(
@@ -151,8 +191,8 @@ extern "C" mxq_status requant_per_token_to_per_tensor(
         partial);
     if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;
   }
-  int64_t blocks = ceil_div(T, 8);
-  if (blocks > 2048) blocks = 2048;
+  int64_t blocks = ceil_div(T, 4 * kRowsPerWave);
+  if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
   requant_apply_kernel<<<(unsigned)blocks, 256, 0, s>>>(
       static_cast<const uint8_t*>(q_in_fp8), ld_in, token_scales, T, H,

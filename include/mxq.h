@@ -52,6 +52,8 @@ extern "C" {
 #define MXQ_ABI_VERSION 1
 #define MXQ_MAX_LOCAL_EXPERTS 1024
 #define MXQ_MAX_TOPK 64
+#define MXQ_MAX_ASSIGNMENTS (1 << 24) /* T*K limit of moe_layout */
+#define MXQ_MAX_HIDDEN 32768 /* moe_scatter_quant stages one row in LDS */
 
 typedef enum {
   MXQ_OK = 0,
@@ -124,7 +126,8 @@ size_t requant_workspace_bytes(int64_t T, int32_t H);
  *                  never written out of bounds; read with moe_read_overflow.
  *   workspace      >= moe_layout_workspace_bytes(T, K, E) bytes, device.
  * Limits: 1 <= E <= MXQ_MAX_LOCAL_EXPERTS, 1 <= K <= MXQ_MAX_TOPK,
- * T*K < 2^31, num_rows < 2^31.  T = 0 is valid (regions empty, m_indices all
+ * num_rows < 2^31 (else MXQ_ERR_INVALID_ARGUMENT), T*K <= MXQ_MAX_ASSIGNMENTS
+ * (else MXQ_ERR_UNSUPPORTED).  T = 0 is valid (regions empty, m_indices all
  * -1). */
 mxq_status moe_layout(const int32_t* topk_ids, int64_t T, int32_t K,
                       int32_t expert_begin, int32_t num_local_experts,
@@ -156,7 +159,8 @@ mxq_status moe_read_overflow(const int32_t* overflow_flag, int32_t* host_value,
  *   scales   uint8 [num_rows, ld_s]; byte g of row d becomes e_g + 127,
  *            ld_s >= H / G (any stride, padded strides allowed).
  * Rows that are no destination are not written (padding keeps whatever the
- * caller left there; consumers skip them through m_indices = -1). */
+ * caller left there; consumers skip them through m_indices = -1).
+ * H <= MXQ_MAX_HIDDEN, else MXQ_ERR_UNSUPPORTED. */
 mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x, int64_t T,
                              int32_t H, const int32_t* src2dst, int32_t K,
                              mxq_scale_fmt fmt, void* q_fp8, int64_t ld_q,

@@ -67,9 +67,9 @@ def test_host_helpers_match_oracle(mxq, ora):
 
 
 def test_workspace_sizes(mxq):
-    assert mxq.moe_layout_workspace_bytes(0, 8, 256) == 0
+    assert mxq.moe_layout_workspace_bytes(0, 8, 256) == (2 * 256 + 1) * 4
     w = mxq.moe_layout_workspace_bytes(8192, 8, 256)
-    assert 0 < w <= 64 * 256 * 4
+    assert 0 < w <= (64 * 256 + 2 * 256 + 1) * 4
     assert mxq.requant_workspace_bytes(16384, 4096) >= 4
 
 
@@ -98,6 +98,8 @@ def test_scatter_quant_validation(mxq):
     assert call(ld_q=264) == INVALID           # fp8 stride not 16-byte
     assert call(T=-1) == INVALID
     assert call(K=65) == INVALID
+    assert call(H=32768 + 128, ld_x=32768 + 128, ld_q=32768 + 128,
+                ld_s=300) == UNSUPPORTED       # row does not fit in LDS
     assert call(T=0) == 0                      # empty batch: nothing to do
     assert call(rows=0, q=None, s=None) == 0
 
@@ -123,6 +125,7 @@ def test_layout_validation(mxq):
     assert call(wsb=4) == WORKSPACE
     assert call(ids=None) == INVALID
     assert call(block=0, rows=1024) == INVALID
+    assert call(T=(1 << 21) + 1, K=8, rows=1 << 30) == UNSUPPORTED  # > 2^24
 
 
 def test_combine_requant_live_validation(mxq):
