@@ -7,16 +7,15 @@
 // slots with masked_m, overflow fails fast).  Slots inside an expert follow
 // ascending flat assignment index t*K + j.
 //
-// Three launches whose grids depend only on T*K, E and num_rows:
+// Two launches whose grids depend only on T*K, E and num_rows:
 //   layout_hist_kernel    one block per chunk of assignments: LDS histogram
 //                         of the chunk's local experts -> cnt[chunk][E].
-//   layout_scan_kernel    one block, one thread per expert: turns the chunk
-//                         counts into each chunk's first slot (in place),
-//                         the totals c_e and, by a block-wide scan of the
-//                         padded sizes, the region starts; publishes counts,
-//                         region starts, masked_m and the overflow flag.
 //   layout_assign_kernel  one block of 16 wavefronts per chunk, plus enough
 //                         blocks for the m_indices fill:
+//     A  every block sums the chunk counts it needs (the totals c_e and the
+//        counts of earlier chunks), with a batch of loads in flight;
+//     B  a block-wide scan of the padded sizes gives the region starts;
+//        block 0 publishes counts, region starts, masked_m and the flag;
 //     C  each wavefront ranks its own steps of 64 assignments: lanes with the
 //        same expert are found with one ballot per key bit (a bit-sliced
 //        multi-split) and a lane's rank among them is the popcount of the
@@ -26,7 +25,7 @@
 //     D  rows are mapped to experts through an LDS table with one entry per
 //        block_e rows (regions start on multiples of block_e), or a binary
 //        search over the region starts when that table would not fit in the
-//        LDS left over (64 KB per block in all).
+//        LDS left over (63 KB per block in all).
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
 
@@ -34,10 +33,10 @@ namespace {
 
 using namespace mxq;
 
-constexpr int kScanBatch = 64;
+constexpr int kScanBatch = 16;
 constexpr int kAssignWaves = 16;
 constexpr int kMaxStepsPerWave = kChunkMax / (64 * kAssignWaves);
-constexpr int kAssignLds = 65536;  // LDS bytes of the assign kernel
+constexpr int kAssignLds = 64512;  // dynamic LDS bytes of the assign kernel
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi(
@@ -61,72 +60,6 @@ __global__ __launch_bounds__(256) void layout_hist_kernel(
     cnt[(int64_t)blockIdx.x * E + i] = hist[i];
 }
 
-// Workspace after this kernel: base[c][e] (first slot of chunk c in expert
-// e, overwriting the counts), tot[e], off[e] (E + 1 entries).
-__global__ __launch_bounds__(1024) void layout_scan_kernel(
-    int32_t* __restrict__ base, int32_t* __restrict__ tot_ws,
-    int32_t* __restrict__ off_ws, int32_t E, int32_t nc, int32_t kind,
-    int32_t block_e, int32_t cap, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ masked_m,
-    int32_t* __restrict__ overflow) {
-  __shared__ int32_t wsum[16];
-  const int e = threadIdx.x;
-  const int lane = e & 63;
-  const int wv = e >> 6;
-  int total = 0;
-  if (e < E) {
-    for (int c0 = 0; c0 < nc; c0 += kScanBatch) {
-      int v[kScanBatch];
-#pragma unroll
-      for (int i = 0; i < kScanBatch; ++i)  // a batch of loads in flight
-        v[i] = base[(int64_t)min(c0 + i, nc - 1) * E + e];
-#pragma unroll
-      for (int i = 0; i < kScanBatch; ++i) {
-        if (c0 + i < nc) {
-          base[(int64_t)(c0 + i) * E + e] = total;
-          total += v[i];
-        }
-      }
-    }
-  }
-  int padded = 0;
-  if (e < E) {
-    if (kind == 0) {
-      padded = (total + block_e - 1) / block_e * block_e;
-    } else {
-      padded = cap;
-    }
-  }
-  // block-wide exclusive scan of the padded sizes (E <= 1024)
-  int incl = padded;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wsum[wv] = incl;
-  __syncthreads();
-  int before = 0;
-  const int nwaves = blockDim.x >> 6;
-  for (int w = 0; w < nwaves; ++w) before += (w < wv) ? wsum[w] : 0;
-  const int start = before + incl - padded;
-  int grand = 0;
-  for (int w = 0; w < nwaves; ++w) grand += wsum[w];
-  if (e < E) {
-    tot_ws[e] = total;
-    off_ws[e] = start;
-    counts[e] = total;
-    offsets[e] = start;
-    if (masked_m != nullptr) masked_m[e] = kind == 1 ? min(total, cap) : total;
-  }
-  if (e == 0) {
-    off_ws[E] = grand;
-    offsets[E] = grand;
-  }
-  const int ovf = (e < E && kind == 1 && total > cap) ? 1 : 0;
-  const int any = __syncthreads_or(ovf);
-  if (e == 0) *overflow = any ? 1 : 0;
-}
-
 // Slots: one block of kAssignWaves wavefronts per chunk.  Each wavefront
 // owns a contiguous run of whole 64-assignment steps; it ranks its lanes
 // within each step (ballot multi-split) and among its own earlier steps, and
@@ -138,16 +71,22 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
     const int32_t* __restrict__ ids, int64_t A, int32_t begin, int32_t E,
     int32_t nbits, int32_t kind, int32_t block_e, int32_t cap,
     int64_t num_rows, int32_t chunk, int32_t nc, int32_t steps_per_wave,
-    int32_t tbl_cap, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ tot_ws, const int32_t* __restrict__ off_ws,
+    int32_t tbl_cap, const int32_t* __restrict__ chunk_cnt,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ masked_m, int32_t* __restrict__ overflow,
     int32_t* __restrict__ m_indices, int32_t* __restrict__ src2dst) {
   extern __shared__ int32_t sm[];
+  __shared__ int32_t wsum[16];
   int32_t* tot = sm;                   // [E]
   int32_t* off = sm + E;               // [E + 1]
   int32_t* cbase = sm + 2 * E + 1;     // [E] first slot of this chunk
   int32_t* tbl = sm + 3 * E + 1;       // [tbl_cap] expert per block_e rows
   // [kAssignWaves][E] per-wavefront counts, then their prefixes (< chunk)
   uint16_t* cnt = reinterpret_cast<uint16_t*>(tbl + tbl_cap);
+  // phase A's partial sums live in the row-table space, which is only used
+  // in phase D (tbl_cap >= 2048 for every E)
+  int32_t* part_all = tbl;         // [nparts][E], nparts * E <= 1024
+  int32_t* part_pre = tbl + 1024;  // [nparts][E]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -165,12 +104,80 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
     const int64_t a = w_begin + st * 64 + lane;
     idb[st] = (st < steps_per_wave && a < w_end) ? ids[a] : 0;
   }
-  for (int i = tid; i < E; i += blockDim.x) {
-    tot[i] = tot_ws[i];
-    off[i] = off_ws[i];
-    cbase[i] = has_chunk ? base[(int64_t)c * E + i] : 0;
+
+  // A: totals and this chunk's first slots from the chunk counts.  Up to
+  // four groups of threads per expert split the chunks; each issues its
+  // loads a batch at a time.
+  {
+    const int er = (E + 63) / 64 * 64;
+    const int nparts = max(1, (int)blockDim.x / er);
+    const int part = tid / er;
+    const int e = tid - part * er;
+    if (part < nparts && e < E) {
+      const int per = (nc + nparts - 1) / nparts;
+      const int c_lo = part * per;
+      const int c_hi = min(nc, c_lo + per);
+      int all = 0, pre = 0;
+      for (int cb0 = c_lo; cb0 < c_hi; cb0 += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i)
+          v[i] = chunk_cnt[(int64_t)min(cb0 + i, c_hi - 1) * E + e];
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+          const int cc = cb0 + i;
+          if (cc < c_hi) {
+            all += v[i];
+            pre += cc < c ? v[i] : 0;
+          }
+        }
+      }
+      part_all[part * E + e] = all;
+      part_pre[part * E + e] = pre;
+    }
+    __syncthreads();
+    int total = 0, first = 0;
+    if (tid < E) {
+      for (int p = 0; p < nparts; ++p) {
+        total += part_all[p * E + tid];
+        first += part_pre[p * E + tid];
+      }
+      tot[tid] = total;
+      cbase[tid] = first;
+    }
+    // B: region starts, a block-wide scan of the padded sizes
+    int padded = 0;
+    if (tid < E)
+      padded = kind == 0 ? (total + block_e - 1) / block_e * block_e : cap;
+    int incl = padded;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int before = 0, grand = 0;
+    const int nwaves = blockDim.x >> 6;
+    for (int w = 0; w < nwaves; ++w) {
+      before += (w < wv) ? wsum[w] : 0;
+      grand += wsum[w];
+    }
+    if (tid < E) off[tid] = before + incl - padded;
+    if (tid == 0) off[E] = grand;
+    if (blockIdx.x == 0) {
+      if (tid < E) {
+        counts[tid] = total;
+        offsets[tid] = before + incl - padded;
+        if (masked_m != nullptr)
+          masked_m[tid] = kind == 1 ? min(total, cap) : total;
+      }
+      if (tid == 0) offsets[E] = grand;
+      const int ovf = (tid < E && kind == 1 && total > cap) ? 1 : 0;
+      const int any = __syncthreads_or(ovf);
+      if (tid == 0) *overflow = any ? 1 : 0;
+    }
   }
-  if (tid == 0) off[E] = off_ws[E];
+  __syncthreads();
   for (int i = tid; i < kAssignWaves * E; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
 
@@ -318,42 +325,36 @@ extern "C" mxq_status moe_layout(
     return MXQ_ERR_INVALID_ARGUMENT;
   const LayoutGeom g = layout_geom(A);
   const size_t need = layout_workspace_bytes(A, E);
-  if (workspace == nullptr || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return MXQ_ERR_WORKSPACE;
 
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   hipStream_t s = as_stream(stream);
-  int32_t* base = static_cast<int32_t*>(workspace);
-  int32_t* tot_ws = base + (size_t)g.nc * E;
-  int32_t* off_ws = tot_ws + E;
+  int32_t* chunk_cnt = static_cast<int32_t*>(workspace);
   const int32_t cap = kind == MXQ_LAYOUT_MASKED ? capacity : 0;
   if (g.nc > 0) {
     layout_hist_kernel<<<g.nc, 256, (size_t)E * sizeof(int32_t), s>>>(
-        topk_ids, A, expert_begin, E, g.chunk, base);
+        topk_ids, A, expert_begin, E, g.chunk, chunk_cnt);
     if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;
   }
-  const int scan_threads = (int)ceil_div(E, 64) * 64;
-  layout_scan_kernel<<<1, scan_threads, 0, s>>>(
-      base, tot_ws, off_ws, E, g.nc, (int32_t)kind, block_e, cap, counts,
-      expert_offsets, masked_m, overflow_flag);
-  if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;
-  // One block per chunk; more blocks (up to 64) if the m_indices fill needs
-  // them.  Each of the 16 wavefronts of a block takes steps_per_wave steps.
+  // One block per chunk (at least one: block 0 publishes the per-expert
+  // outputs); more blocks (up to 64) if the m_indices fill needs them.
+  // Each of the 16 wavefronts of a block takes steps_per_wave steps.
   const int32_t steps_per_wave =
       (int32_t)ceil_div(ceil_div(g.chunk, 64), kAssignWaves);
-  int64_t blocks = g.nc;
+  int64_t blocks = g.nc > 0 ? g.nc : 1;
   if (m_indices != nullptr) {
     int64_t fill_blocks = ceil_div(num_rows, 4096);
     if (fill_blocks > 64) fill_blocks = 64;
     if (fill_blocks > blocks) blocks = fill_blocks;
   }
-  if (blocks == 0) return MXQ_OK;
   const size_t fixed = (size_t)(3 * E + 1) * sizeof(int32_t) +
                        (size_t)kAssignWaves * E * sizeof(uint16_t);
   const int32_t tbl_cap = (int32_t)((kAssignLds - fixed) / sizeof(int32_t));
   layout_assign_kernel<<<(unsigned)blocks, 1024, kAssignLds, s>>>(
       topk_ids, A, expert_begin, E, nbits, (int32_t)kind, block_e, cap,
-      num_rows, g.chunk, g.nc, steps_per_wave, tbl_cap, base, tot_ws, off_ws,
-      m_indices, src2dst);
+      num_rows, g.chunk, g.nc, steps_per_wave, tbl_cap, chunk_cnt, counts,
+      expert_offsets, masked_m, overflow_flag, m_indices, src2dst);
   return launch_status();
 }

@@ -69,12 +69,10 @@ inline LayoutGeom layout_geom(int64_t A) {
   return g;
 }
 
-// Workspace: per-chunk counts (then first slots) [nc][E], totals [E] and
-// region starts [E + 1].
+// Workspace: per-chunk expert counts [nc][E] (none without assignments).
 inline size_t layout_workspace_bytes(int64_t A, int32_t E) {
   LayoutGeom g = layout_geom(A);
-  const size_t e = (size_t)(E > 0 ? E : 0);
-  return ((size_t)g.nc * e + 2 * e + 1) * sizeof(int32_t);
+  return (size_t)g.nc * (size_t)(E > 0 ? E : 0) * sizeof(int32_t);
 }
 
 }  // namespace mxq
