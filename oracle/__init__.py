@@ -80,6 +80,13 @@ def lib() -> ctypes.CDLL:
                                        _i64]),
             "ora_combine_f64": (None, [_p, _i64, _p, _p, _i64, _i32, _i32, _p,
                                        _p, _i64]),
+            "ora_m_indices_from_psum": (None, [_p, _i32, _i32, _i64, _p]),
+            "ora_expand_to_masked_slab": (
+                _i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _i32, _i32, _p,
+                       _i32, _i32, _i32, _p, _i64, _p, _i64, _i64, _p]),
+            "ora_masked_slab_to_expand": (
+                None, [_p, _i64, _i32, _p, _p, _i32, _i32, _i32, _p, _p, _i64,
+                       _i64]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -265,3 +272,70 @@ def combine_f64(y_bf16, src2dst, weights):
     lib().ora_combine_f64(_ptr(y), H, _ptr(d), _ptr(w), T, K, H, _ptr(out),
                           _ptr(mag), H)
     return out, mag
+
+
+# ------------------------------------------------- psum (expanded) layouts
+
+def m_indices_from_psum(psum, align: int, num_rows: int):
+    p = _c(psum, np.int32)
+    m = np.empty(num_rows, np.int32)
+    lib().ora_m_indices_from_psum(_ptr(p), p.size, align, num_rows, _ptr(m))
+    return m
+
+
+def expand_to_masked_slab(x_rows: np.ndarray, psum, align: int, max_m: int,
+                          scales: np.ndarray | None = None,
+                          scales_col_major: bool = False, slab=None,
+                          slab_scales=None):
+    """x_rows: [rows, row_bytes] uint8 (any payload as bytes); scales:
+    [rows, s_cols] array of 1- or 4-byte elements, stored row-major or (with
+    scales_col_major) as the transpose [s_cols, rows].  Returns (slab
+    [E, max_m, row_bytes], slab_scales [E, max_m, s_cols] or None, masked_m,
+    flags)."""
+    x = _c(x_rows, np.uint8)
+    rows, rb = x.shape
+    p = _c(psum, np.int32)
+    E = p.size
+    if slab is None:
+        slab = np.zeros((E * max_m, rb), np.uint8)
+    masked_m = np.empty(E, np.int32)
+    xs_ptr = ss_ptr = 0
+    xs_rs = xs_cs = ss_rs = ss_cs = s_cols = s_elem = 0
+    if scales is not None:
+        sc = np.ascontiguousarray(scales)
+        s_elem = sc.dtype.itemsize
+        if scales_col_major:
+            s_cols = sc.shape[0]
+            xs_rs, xs_cs = s_elem, sc.shape[1] * s_elem
+        else:
+            s_cols = sc.shape[1]
+            xs_rs, xs_cs = s_cols * s_elem, s_elem
+        if slab_scales is None:
+            slab_scales = np.zeros((E * max_m, s_cols), sc.dtype)
+        ss_rs, ss_cs = s_cols * s_elem, s_elem
+        xs_ptr, ss_ptr = _ptr(sc), _ptr(slab_scales)
+    flags = lib().ora_expand_to_masked_slab(
+        _ptr(x), rb, rows, rb, xs_ptr, xs_rs, xs_cs, s_cols, s_elem, _ptr(p),
+        E, align, max_m, _ptr(slab), rb, ss_ptr, ss_rs, ss_cs,
+        _ptr(masked_m))
+    return slab, slab_scales, masked_m, int(flags)
+
+
+def masked_slab_to_expand(slab_bf16: np.ndarray, masked_m, psum, align: int,
+                          max_m: int, weights=None, out=None,
+                          out_rows: int | None = None):
+    """slab_bf16: [E*max_m, H] bf16 bits.  out (bf16 bits) is updated in
+    place on real rows only."""
+    sl = _c(slab_bf16, np.uint16)
+    H = sl.shape[1]
+    p = _c(psum, np.int32)
+    mm = _c(masked_m, np.int32)
+    E = p.size
+    if out is None:
+        out = np.zeros((out_rows, H), np.uint16)
+    assert out.flags.c_contiguous
+    w = None if weights is None else _c(weights, np.float32)
+    lib().ora_masked_slab_to_expand(_ptr(sl), H, H, _ptr(mm), _ptr(p), E,
+                                    align, max_m, 0 if w is None else _ptr(w),
+                                    _ptr(out), out.shape[1], out.shape[0])
+    return out

@@ -437,3 +437,94 @@ void ora_combine_f64(const uint16_t* y, int64_t ld_y, const int32_t* src2dst,
     }
   }
 }
+
+/* ------------------------------------------- psum (expanded) layout repack */
+
+/* Expanded layout of a dispatcher [P3 Key source snippets, _build_layout]:
+ * expert e owns rows [start_e, psum[e]) with start_e = align(psum[e-1]) and
+ * psum[-1] = 0.  A psum entry below its start gives an empty expert. */
+static int64_t psum_start(const int32_t* psum, int32_t e, int32_t align) {
+  int64_t prev = e == 0 ? 0 : psum[e - 1];
+  if (prev < 0) prev = 0;
+  return (prev + align - 1) / align * align;
+}
+
+static int64_t psum_count(const int32_t* psum, int32_t e, int32_t align) {
+  int64_t c = (int64_t)psum[e] - psum_start(psum, e, align);
+  return c > 0 ? c : 0;
+}
+
+/* m_indices of the contiguous GEMM rebuilt from psum [P3 Implementation
+ * breakdown item 3 (m_indices from psum with a static grid); Review
+ * highlights item 1 (the tail of each expert's range is masked, so a row
+ * past psum[e] never gets e)]: m[r] = e on real rows, -1 elsewhere. */
+void ora_m_indices_from_psum(const int32_t* psum, int32_t E, int32_t align,
+                             int64_t num_rows, int32_t* m_indices) {
+  for (int64_t r = 0; r < num_rows; ++r) m_indices[r] = -1;
+  for (int32_t e = 0; e < E; ++e) {
+    int64_t s = psum_start(psum, e, align), c = psum_count(psum, e, align);
+    for (int64_t j = 0; j < c && s + j < num_rows; ++j) m_indices[s + j] = e;
+  }
+}
+
+/* Expanded -> masked slab [P3 Implementation breakdown item 3; Key source
+ * snippets (_check_expand_roundtrip: masked_m equals the counts, slab row j
+ * of expert e equals expanded row start_e + j); Review highlights (overflow
+ * fails fast)].  Rows are opaque byte strings of row_bytes; scale entries
+ * (elem bytes each, s_cols per row) are addressed with explicit row and
+ * column strides on both sides, so column-major packed sources work.
+ * Copies min(count, max_m) rows of each expert whose source rows exist;
+ * masked_m[e] = that number; returns flags: 1 = some count > max_m,
+ * 2 = some real row lies past src_rows. */
+int32_t ora_expand_to_masked_slab(
+    const uint8_t* x, int64_t ld_x, int64_t src_rows, int64_t row_bytes,
+    const uint8_t* xs, int64_t xs_rs, int64_t xs_cs, int32_t s_cols,
+    int32_t s_elem, const int32_t* psum, int32_t E, int32_t align,
+    int32_t max_m, uint8_t* slab, int64_t ld_slab, uint8_t* slab_s,
+    int64_t ss_rs, int64_t ss_cs, int32_t* masked_m) {
+  int32_t flags = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    int64_t s = psum_start(psum, e, align), c = psum_count(psum, e, align);
+    if (c > max_m) { flags |= 1; c = max_m; }
+    if (s + c > src_rows) { flags |= 2; c = src_rows > s ? src_rows - s : 0; }
+    masked_m[e] = (int32_t)c;
+    for (int64_t j = 0; j < c; ++j) {
+      int64_t dr = (int64_t)e * max_m + j;
+      memcpy(slab + dr * ld_slab, x + (s + j) * ld_x, (size_t)row_bytes);
+      if (xs && slab_s)
+        for (int32_t g = 0; g < s_cols; ++g)
+          memcpy(slab_s + dr * ss_rs + g * ss_cs,
+                 xs + (s + j) * xs_rs + g * xs_cs, (size_t)s_elem);
+    }
+  }
+  return flags;
+}
+
+/* Masked slab -> expanded with the top-k weights fused on real rows only
+ * [P3 Implementation breakdown item 3; Key source snippets
+ * (_check_expand_roundtrip)]: out[start_e + j] = bf16(w[start_e + j] *
+ * slab[e][j]) (one fp32 product, nearest-even rounding; w = NULL copies the
+ * row) for j < masked_m[e]; every other expanded row is left untouched. */
+void ora_masked_slab_to_expand(const uint16_t* slab, int64_t ld_slab,
+                               int32_t H, const int32_t* masked_m,
+                               const int32_t* psum, int32_t E, int32_t align,
+                               int32_t max_m, const float* w, uint16_t* out,
+                               int64_t ld_out, int64_t out_rows) {
+  for (int32_t e = 0; e < E; ++e) {
+    int64_t s = psum_start(psum, e, align);
+    int64_t c = masked_m[e];
+    if (c > max_m) c = max_m;
+    for (int64_t j = 0; j < c && s + j < out_rows; ++j) {
+      const uint16_t* src = slab + ((int64_t)e * max_m + j) * ld_slab;
+      uint16_t* dst = out + (s + j) * ld_out;
+      for (int32_t h = 0; h < H; ++h) {
+        if (w) {
+          float v = bf16_to_float(src[h]) * w[s + j];
+          dst[h] = ora_bf16_round(v);
+        } else {
+          dst[h] = src[h];
+        }
+      }
+    }
+  }
+}
