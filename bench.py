@@ -376,6 +376,47 @@ def other_rows(torch, mxq, si, dev):
                                "across the two passes and back-to-back calls"}
     del qi, qo
 
+    # psum (expanded) layout repack at the decode shape: the dispatcher's
+    # expanded rows (counts of the decode routing, 128-aligned) -> masked
+    # slab [32, 128, 7168] fp8 + 56 UE8M0 bytes, and the bf16 slab back to
+    # expanded rows with the top-k weights applied
+    counts = mxq.moe_layout(ids, 0, 32, "masked", capacity=128)["counts"]
+    cnt = counts.cpu().numpy().astype(np.int64)
+    starts = np.zeros(32, np.int64)
+    psum_h = np.zeros(32, np.int32)
+    prev = 0
+    for e in range(32):
+        starts[e] = -(-prev // 128) * 128
+        psum_h[e] = starts[e] + cnt[e]
+        prev = psum_h[e]
+    total = int(-(-prev // 128) * 128)
+    psum = torch.from_numpy(psum_h).to(dev)
+    xr = torch.randint(0, 255, (total, 7168), dtype=torch.uint8, device=dev)
+    xsc = torch.randint(100, 140, (total, 56), dtype=torch.uint8, device=dev)
+    slab = torch.empty((32 * 128, 7168), dtype=torch.uint8, device=dev)
+    slab_s = torch.empty((32 * 128, 56), dtype=torch.uint8, device=dev)
+    us_e = time_calls(torch, lambda: mxq.moe_expand_to_masked_slab(
+        xr, psum, 128, 128, scales=xsc, slab=slab, slab_scales=slab_s))
+    _, _, mm, _ = mxq.moe_expand_to_masked_slab(xr, psum, 128, 128,
+                                                 scales=xsc, slab=slab,
+                                                 slab_scales=slab_s)
+    ys = si.gaussian_bf16_device(206, (32 * 128, 7168), dev)
+    wexp = torch.rand(total, device=dev)
+    oexp = torch.zeros((total, 7168), dtype=torch.bfloat16, device=dev)
+    us_b = time_calls(torch, lambda: mxq.moe_masked_slab_to_expand(
+        ys, mm, psum, 128, 128, weights=wexp, out=oexp))
+    us_m = time_calls(torch, lambda: mxq.moe_m_indices_from_psum(
+        psum, total, 128))
+    real = int(cnt.sum())
+    rows["psum_repack"] = {
+        "workload": "decode expanded layout: %d real rows in %d (32 experts, "
+                    "128-aligned) <-> slab [32, 128, 7168]" % (real, total),
+        "expand_to_masked_slab_us": round(us_e, 2),
+        "expand_bytes": real * 2 * (7168 + 56) + 32 * 8,
+        "masked_slab_to_expand_us": round(us_b, 2),
+        "slab_to_expand_bytes": real * (2 * 7168 * 2 + 4),
+        "m_indices_from_psum_us": round(us_m, 2)}
+
     # large combine: 16384 tokens x 4096 from 147328 rows, top-8 of 128
     cids, cw = si.large_combine_routing()
     idsd = torch.from_numpy(cids).to(dev)

@@ -26,7 +26,8 @@ __all__ = [
     "moe_layout", "moe_read_overflow", "moe_scatter_quant",
     "mx_quant_live_rows", "live_rows_view",
     "requant_per_token_to_per_tensor", "moe_combine", "mxq_e4m3_encode_f32",
-    "mxq_abi_version",
+    "mxq_abi_version", "moe_m_indices_from_psum", "moe_expand_to_masked_slab",
+    "moe_masked_slab_to_expand",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +59,12 @@ _SIGNATURES = {
     "moe_combine": (_i32, [_p, _i64, _i64, _p, _p, _i64, _i32, _i32, _p, _i64,
                            _i32, _p]),
     "mxq_e4m3_encode_f32": (_i32, [_p, _i64, _p, _p]),
+    "moe_m_indices_from_psum": (_i32, [_p, _i32, _i32, _i64, _p, _p]),
+    "moe_expand_to_masked_slab": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64,
+                                         _i32, _i32, _p, _i32, _i32, _i32, _p,
+                                         _i64, _p, _i64, _i64, _p, _p, _p]),
+    "moe_masked_slab_to_expand": (_i32, [_p, _i64, _i32, _p, _p, _i32, _i32,
+                                         _i32, _p, _p, _i64, _i64, _p]),
     "mxq_status_string": (ctypes.c_char_p, [_i32]),
     "mxq_abi_version": (_i32, []),
 }
@@ -385,4 +392,102 @@ def mxq_e4m3_encode_f32(x: torch.Tensor) -> torch.Tensor:
     st = lib().mxq_e4m3_encode_f32(_ptr(xc), xc.numel(), _ptr(out),
                                    _stream(xc))
     _check("mxq_e4m3_encode_f32", st)
+    return out
+
+
+# ---------------------------------------------------- psum (expanded) layout
+
+def _psum(psum: torch.Tensor) -> torch.Tensor:
+    _dev(psum, "psum")
+    if psum.dtype != torch.int32 or psum.dim() != 1 or \
+            not psum.is_contiguous():
+        raise ValueError("psum must be contiguous int32 [E]")
+    return psum
+
+
+def moe_m_indices_from_psum(psum: torch.Tensor, num_rows: int,
+                            align: int = 128,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """m_indices [num_rows] of the contiguous GEMM from a dispatcher's
+    psum: e on rows [align(psum[e-1]), psum[e]), -1 elsewhere."""
+    p = _psum(psum)
+    if out is None:
+        out = torch.empty(num_rows, dtype=torch.int32, device=p.device)
+    st = lib().moe_m_indices_from_psum(_ptr(p), p.numel(), align, num_rows,
+                                       _ptr(out), _stream(p))
+    _check("moe_m_indices_from_psum", st)
+    return out
+
+
+def moe_expand_to_masked_slab(x: torch.Tensor, psum: torch.Tensor,
+                              max_m: int, align: int = 128,
+                              scales: torch.Tensor | None = None,
+                              scales_col_major: bool = False,
+                              slab: torch.Tensor | None = None,
+                              slab_scales: torch.Tensor | None = None):
+    """Expanded rows ``x [rows, cols]`` (any element type) -> masked slab
+    ``[E * max_m, cols]``.  ``scales`` is ``[rows, s_cols]``, or its
+    transpose stored as ``[s_cols, rows]`` when ``scales_col_major``.
+    Returns ``(slab, slab_scales, masked_m, flags)`` (device tensors)."""
+    _dev(x, "x")
+    p = _psum(psum)
+    E = p.numel()
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError("x must be 2-D with unit column stride")
+    esz = x.element_size()
+    rows, cols = x.shape
+    ld_x = (x.stride(0) if rows > 1 else cols) * esz
+    if slab is None:
+        slab = torch.empty((E * max_m, cols), dtype=x.dtype, device=x.device)
+    ld_slab = (slab.stride(0) if slab.shape[0] > 1 else cols) * esz
+    masked_m = torch.empty(E, dtype=torch.int32, device=x.device)
+    flags = torch.empty(1, dtype=torch.int32, device=x.device)
+    xs_rs = xs_cs = ss_rs = ss_cs = s_cols = s_elem = 0
+    if scales is not None:
+        _dev(scales, "scales")
+        s_elem = scales.element_size()
+        if scales_col_major:
+            s_cols = scales.shape[0]
+            xs_rs, xs_cs = scales.stride(1) * s_elem, scales.stride(0) * s_elem
+        else:
+            s_cols = scales.shape[1]
+            xs_rs, xs_cs = scales.stride(0) * s_elem, scales.stride(1) * s_elem
+        if slab_scales is None:
+            slab_scales = torch.empty((E * max_m, s_cols), dtype=scales.dtype,
+                                      device=x.device)
+        ss_rs = slab_scales.stride(0) * s_elem
+        ss_cs = slab_scales.stride(1) * s_elem
+    st = lib().moe_expand_to_masked_slab(
+        _ptr(x), ld_x, rows, cols * esz, _ptr(scales), xs_rs, xs_cs, s_cols,
+        s_elem, _ptr(p), E, align, max_m, _ptr(slab), ld_slab,
+        _ptr(slab_scales), ss_rs, ss_cs, _ptr(masked_m), _ptr(flags),
+        _stream(x))
+    _check("moe_expand_to_masked_slab", st)
+    return slab, slab_scales, masked_m, flags
+
+
+def moe_masked_slab_to_expand(slab: torch.Tensor, masked_m: torch.Tensor,
+                              psum: torch.Tensor, max_m: int,
+                              align: int = 128,
+                              weights: torch.Tensor | None = None,
+                              out: torch.Tensor | None = None,
+                              out_rows: int | None = None) -> torch.Tensor:
+    """bf16 slab ``[E * max_m, H]`` -> expanded rows of ``out [rows, H]``
+    (real rows only), multiplied by ``weights [rows]`` when given."""
+    _dev(slab, "slab")
+    p = _psum(psum)
+    ld_slab = _rows(slab, "slab", (torch.bfloat16,))
+    H = slab.shape[1]
+    if out is None:
+        out = torch.zeros((out_rows, H), dtype=torch.bfloat16,
+                          device=slab.device)
+    ld_out = _rows(out, "out", (torch.bfloat16,))
+    if weights is not None and (weights.dtype != torch.float32 or
+                                not weights.is_contiguous() or
+                                weights.numel() < out.shape[0]):
+        raise ValueError("weights must be contiguous float32 [rows]")
+    st = lib().moe_masked_slab_to_expand(
+        _ptr(slab), ld_slab, H, _ptr(masked_m), _ptr(p), p.numel(), align,
+        max_m, _ptr(weights), _ptr(out), ld_out, out.shape[0], _stream(slab))
+    _check("moe_masked_slab_to_expand", st)
     return out

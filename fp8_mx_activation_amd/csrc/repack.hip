@@ -1,0 +1,245 @@
+// Repack between a dispatcher's expanded (psum) layout and the masked slab.
+//
+// The expanded layout is the one the DeepEPv2 page describes (key source
+// snippets, _build_layout): expert e owns rows [start_e, psum[e]) with
+// start_e = align(psum[e-1]) and psum[-1] = 0.  Three operations from that
+// page (implementation breakdown item 3; review highlights):
+//   moe_m_indices_from_psum    m_indices of the contiguous GEMM, with the
+//                              tail of every range masked to -1;
+//   moe_expand_to_masked_slab  expanded rows (and their scales, copied by
+//                              explicit source strides) -> [E, max_m] slab
+//                              plus masked_m; over-capacity experts raise a
+//                              flag instead of being truncated silently;
+//   moe_masked_slab_to_expand  slab -> expanded rows with the top-k weight
+//                              applied on real rows only.
+// All grids depend only on host arguments (E, max_m, num_rows), so every
+// call can be captured in a hipGraph.
+#include "mxq_device.hpp"
+#include "mxq_host.hpp"
+
+namespace {
+
+using namespace mxq;
+
+constexpr int kRowsPerBlock = 8;
+
+__device__ __forceinline__ int64_t psum_start(const int32_t* psum, int e,
+                                              int32_t align) {
+  int64_t prev = e == 0 ? 0 : (int64_t)psum[e - 1];
+  if (prev < 0) prev = 0;
+  return (prev + align - 1) / align * align;
+}
+
+__device__ __forceinline__ int64_t psum_count(const int32_t* psum, int e,
+                                              int32_t align) {
+  const int64_t c = (int64_t)psum[e] - psum_start(psum, e, align);
+  return c > 0 ? c : 0;
+}
+
+__global__ __launch_bounds__(1024) void m_indices_from_psum_kernel(
+    const int32_t* __restrict__ psum, int32_t E, int32_t align,
+    int64_t num_rows, int32_t* __restrict__ m_indices) {
+  extern __shared__ int64_t rng[];  // [E] starts, [E] ends
+  int64_t* st = rng;
+  int64_t* en = rng + E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    st[e] = psum_start(psum, e, align);
+    en[e] = st[e] + psum_count(psum, e, align);
+  }
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+       r < num_rows; r += stride) {
+    int32_t v = -1;
+    if (r >= st[0]) {
+      int lo = 0, hi = E - 1;  // largest e with start_e <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (st[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      if (r < en[lo]) v = lo;
+    }
+    m_indices[r] = v;
+  }
+}
+
+// Block (e, b) copies rows [b*kRowsPerBlock, (b+1)*kRowsPerBlock) of expert
+// e's slab.  Row payloads move as 16-byte vectors, scale entries one by one
+// through their strides.
+__global__ __launch_bounds__(256) void expand_to_slab_kernel(
+    const uint8_t* __restrict__ x, int64_t ld_x, int64_t src_rows,
+    int64_t row_bytes, const uint8_t* __restrict__ xs, int64_t xs_rs,
+    int64_t xs_cs, int32_t s_cols, int32_t s_elem,
+    const int32_t* __restrict__ psum, int32_t E, int32_t align, int32_t max_m,
+    uint8_t* __restrict__ slab, int64_t ld_slab, uint8_t* __restrict__ ss,
+    int64_t ss_rs, int64_t ss_cs, int32_t* __restrict__ masked_m,
+    int32_t* __restrict__ flags) {
+  const int e = blockIdx.x / ((max_m + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int b = blockIdx.x % ((max_m + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int64_t s = psum_start(psum, e, align);
+  int64_t c = psum_count(psum, e, align);
+  if (c > max_m) c = max_m;
+  if (s + c > src_rows) c = src_rows > s ? src_rows - s : 0;
+  if (b == 0 && threadIdx.x == 0) masked_m[e] = (int32_t)c;
+  if (blockIdx.x == 0) {  // one writer for the flags word
+    int f = 0;
+    for (int ee = threadIdx.x; ee < E; ee += blockDim.x) {
+      const int64_t s2 = psum_start(psum, ee, align);
+      int64_t c2 = psum_count(psum, ee, align);
+      if (c2 > max_m) { f |= 1; c2 = max_m; }
+      if (s2 + c2 > src_rows) f |= 2;
+    }
+    const int any1 = __syncthreads_or(f & 1);
+    const int any2 = __syncthreads_or(f & 2);
+    if (threadIdx.x == 0) *flags = (any1 ? 1 : 0) | (any2 ? 2 : 0);
+  }
+  const int64_t j0 = (int64_t)b * kRowsPerBlock;
+  const int64_t j1 = min(j0 + kRowsPerBlock, c);
+  const int64_t nvec = row_bytes / 16;
+  for (int64_t j = j0; j < j1; ++j) {
+    const uint8_t* src = x + (s + j) * ld_x;
+    uint8_t* dst = slab + ((int64_t)e * max_m + j) * ld_slab;
+    for (int64_t v = threadIdx.x; v < nvec; v += blockDim.x)
+      store16(dst + v * 16, load16(src + v * 16));
+    if (xs != nullptr) {
+      const uint8_t* srs = xs + (s + j) * xs_rs;
+      uint8_t* drs = ss + ((int64_t)e * max_m + j) * ss_rs;
+      for (int g = threadIdx.x; g < s_cols; g += blockDim.x) {
+        if (s_elem == 4) {
+          uint32_t w;
+          __builtin_memcpy(&w, srs + g * xs_cs, 4);
+          __builtin_memcpy(drs + g * ss_cs, &w, 4);
+        } else {
+          drs[g * ss_cs] = srs[g * xs_cs];
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t scale_bf16x2(uint32_t v, float w) {
+  const float a = __uint_as_float(v << 16) * w;
+  const float b = __uint_as_float(v & 0xFFFF0000u) * w;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+template <bool WEIGHTED>
+__global__ __launch_bounds__(256) void slab_to_expand_kernel(
+    const uint16_t* __restrict__ slab, int64_t ld_slab, int32_t H,
+    const int32_t* __restrict__ masked_m, const int32_t* __restrict__ psum,
+    int32_t align, int32_t max_m, const float* __restrict__ w,
+    uint16_t* __restrict__ out, int64_t ld_out, int64_t out_rows) {
+  const int nb = (max_m + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int e = blockIdx.x / nb;
+  const int b = blockIdx.x % nb;
+  const int64_t s = psum_start(psum, e, align);
+  int64_t c = masked_m[e];
+  if (c > max_m) c = max_m;
+  const int64_t j0 = (int64_t)b * kRowsPerBlock;
+  const int64_t j1 = min(j0 + kRowsPerBlock, c);
+  for (int64_t j = j0; j < j1 && s + j < out_rows; ++j) {
+    const uint16_t* src = slab + ((int64_t)e * max_m + j) * ld_slab;
+    uint16_t* dst = out + (s + j) * ld_out;
+    const float wj = WEIGHTED ? w[s + j] : 1.0f;
+    for (int col = threadIdx.x * 8; col < H; col += blockDim.x * 8) {
+      u32x4 v = load16(src + col);
+      if (WEIGHTED) {
+        v.x = scale_bf16x2(v.x, wj);
+        v.y = scale_bf16x2(v.y, wj);
+        v.z = scale_bf16x2(v.z, wj);
+        v.w = scale_bf16x2(v.w, wj);
+      }
+      store16(dst + col, v);
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" mxq_status moe_m_indices_from_psum(const int32_t* psum, int32_t E,
+                                              int32_t align, int64_t num_rows,
+                                              int32_t* m_indices,
+                                              void* stream) {
+  if (E < 1 || E > MXQ_MAX_LOCAL_EXPERTS || align < 1 || num_rows < 0 ||
+      num_rows > INT32_MAX)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (num_rows == 0) return MXQ_OK;
+  if (psum == nullptr || m_indices == nullptr) return MXQ_ERR_INVALID_ARGUMENT;
+  int64_t blocks = ceil_div(num_rows, 1024 * 4);
+  if (blocks > 256) blocks = 256;
+  m_indices_from_psum_kernel<<<(unsigned)blocks, 1024,
+                               (size_t)2 * E * sizeof(int64_t),
+                               as_stream(stream)>>>(psum, E, align, num_rows,
+                                                    m_indices);
+  return launch_status();
+}
+
+extern "C" mxq_status moe_expand_to_masked_slab(
+    const void* x, int64_t ld_x, int64_t src_rows, int64_t row_bytes,
+    const void* x_scales, int64_t xs_row_stride, int64_t xs_col_stride,
+    int32_t scale_cols, int32_t scale_elem_bytes, const int32_t* psum,
+    int32_t E, int32_t align, int32_t max_m, void* slab, int64_t ld_slab,
+    void* slab_scales, int64_t ss_row_stride, int64_t ss_col_stride,
+    int32_t* masked_m, int32_t* flags, void* stream) {
+  if (E < 1 || E > MXQ_MAX_LOCAL_EXPERTS || align < 1 || max_m < 1 ||
+      src_rows < 0 || row_bytes < 0)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (row_bytes % 16 != 0) return MXQ_ERR_UNSUPPORTED;
+  if (psum == nullptr || masked_m == nullptr || flags == nullptr ||
+      slab == nullptr)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (src_rows > 0 && x == nullptr) return MXQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || ld_x % 16 != 0 || ld_x < row_bytes ||
+      !aligned16(slab) || ld_slab % 16 != 0 || ld_slab < row_bytes)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (x_scales != nullptr) {
+    if (slab_scales == nullptr || scale_cols < 0 ||
+        (scale_elem_bytes != 1 && scale_elem_bytes != 4))
+      return MXQ_ERR_INVALID_ARGUMENT;
+    if (scale_elem_bytes == 4 &&
+        (((reinterpret_cast<uintptr_t>(x_scales) |
+           reinterpret_cast<uintptr_t>(slab_scales)) & 3) != 0 ||
+         (xs_row_stride | xs_col_stride | ss_row_stride | ss_col_stride) % 4))
+      return MXQ_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t blocks = (int64_t)E * ceil_div(max_m, kRowsPerBlock);
+  if (blocks > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
+  expand_to_slab_kernel<<<(unsigned)blocks, 256, 0, as_stream(stream)>>>(
+      static_cast<const uint8_t*>(x), ld_x, src_rows, row_bytes,
+      static_cast<const uint8_t*>(x_scales), xs_row_stride, xs_col_stride,
+      scale_cols, scale_elem_bytes, psum, E, align, max_m,
+      static_cast<uint8_t*>(slab), ld_slab, static_cast<uint8_t*>(slab_scales),
+      ss_row_stride, ss_col_stride, masked_m, flags);
+  return launch_status();
+}
+
+extern "C" mxq_status moe_masked_slab_to_expand(
+    const void* slab_bf16, int64_t ld_slab, int32_t H, const int32_t* masked_m,
+    const int32_t* psum, int32_t E, int32_t align, int32_t max_m,
+    const float* weights, void* out_bf16, int64_t ld_out, int64_t out_rows,
+    void* stream) {
+  if (E < 1 || E > MXQ_MAX_LOCAL_EXPERTS || align < 1 || max_m < 1 ||
+      H <= 0 || H % 8 != 0 || out_rows < 0)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (out_rows == 0) return MXQ_OK;
+  if (slab_bf16 == nullptr || masked_m == nullptr || psum == nullptr ||
+      out_bf16 == nullptr)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(slab_bf16) || (ld_slab * 2) % 16 != 0 || ld_slab < H ||
+      !aligned16(out_bf16) || (ld_out * 2) % 16 != 0 || ld_out < H)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  const int64_t blocks = (int64_t)E * ceil_div(max_m, kRowsPerBlock);
+  if (blocks > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
+  const uint16_t* sl = static_cast<const uint16_t*>(slab_bf16);
+  uint16_t* o = static_cast<uint16_t*>(out_bf16);
+  if (weights != nullptr)
+    slab_to_expand_kernel<true><<<(unsigned)blocks, 256, 0, as_stream(stream)>>>(
+        sl, ld_slab, H, masked_m, psum, align, max_m, weights, o, ld_out,
+        out_rows);
+  else
+    slab_to_expand_kernel<false><<<(unsigned)blocks, 256, 0, as_stream(stream)>>>(
+        sl, ld_slab, H, masked_m, psum, align, max_m, nullptr, o, ld_out,
+        out_rows);
+  return launch_status();
+}

@@ -220,6 +220,60 @@ mxq_status moe_combine(const void* y_bf16, int64_t ld_y, int64_t num_rows,
                        int64_t T, int32_t K, int32_t H, void* out,
                        int64_t ld_out, mxq_out_dtype out_dtype, void* stream);
 
+/* ------------------------------------------------ psum (expanded) layout */
+
+/* The expanded layout a dispatcher hands over [P3 Key source snippets,
+ * _build_layout]: expert e owns rows [start_e, psum[e]) with
+ * start_e = align(psum[e-1]), psum[-1] = 0; psum (device, int32 [E]) must be
+ * non-decreasing (other values give unspecified but in-bounds results). */
+
+/* m_indices of the contiguous grouped GEMM from psum [P3 impl. item 3
+ * (m_indices from psum, static grid); Review highlights item 1 (each range's
+ * tail is masked)]: m_indices[r] = e for r in [start_e, psum[e]), -1 for
+ * every other r < num_rows.  m_indices int32 [num_rows], device. */
+mxq_status moe_m_indices_from_psum(const int32_t* psum, int32_t E,
+                                   int32_t align, int64_t num_rows,
+                                   int32_t* m_indices, void* stream);
+
+/* Expanded rows -> masked slab [P3 impl. item 3 (scales copied by the
+ * source's pack-dim stride); Key source snippets (masked_m equals the
+ * counts; slab row j of expert e is expanded row start_e + j); Review
+ * highlights (over-capacity must fail fast, never truncate silently)].
+ *
+ *   x            src_rows rows of row_bytes bytes, row stride ld_x bytes
+ *                (any payload: fp8, bf16, ...); row_bytes % 16 == 0.
+ *   x_scales     optional: scale_cols entries of scale_elem_bytes (1 or 4)
+ *                per row, entry (r, g) at r*xs_row_stride + g*xs_col_stride
+ *                bytes (row- or column-major sources alike).
+ *   slab         [E * max_m] rows, stride ld_slab bytes; slab_scales entry
+ *                (row, g) at row*ss_row_stride + g*ss_col_stride bytes.
+ *   masked_m     int32 [E]: rows copied for expert e, min(count, max_m),
+ *                also limited to rows that exist in the source.
+ *   flags        int32 [1]: bit 0 = some count > max_m, bit 1 = some range
+ *                reaches past src_rows; read with moe_read_overflow.
+ * Only rows [0, masked_m[e]) of each expert's slab are written. */
+mxq_status moe_expand_to_masked_slab(
+    const void* x, int64_t ld_x, int64_t src_rows, int64_t row_bytes,
+    const void* x_scales, int64_t xs_row_stride, int64_t xs_col_stride,
+    int32_t scale_cols, int32_t scale_elem_bytes, const int32_t* psum,
+    int32_t E, int32_t align, int32_t max_m, void* slab, int64_t ld_slab,
+    void* slab_scales, int64_t ss_row_stride, int64_t ss_col_stride,
+    int32_t* masked_m, int32_t* flags, void* stream);
+
+/* Masked slab -> expanded rows with the top-k weights applied on real rows
+ * only [P3 impl. item 3 (top-k weights fused in the kernel); Key source
+ * snippets (round trip expanded <-> slab)].  For j < min(masked_m[e], max_m)
+ * and start_e + j < out_rows: out[start_e + j] = bf16(w[start_e + j] *
+ * slab[e*max_m + j]) (fp32 product, one nearest-even rounding), or a plain
+ * copy when weights is NULL.  Every other output row is left untouched.
+ *   slab_bf16 [E * max_m, ld_slab], out_bf16 [out_rows, ld_out] (elements),
+ *   weights fp32 [out_rows] or NULL; H % 8 == 0. */
+mxq_status moe_masked_slab_to_expand(
+    const void* slab_bf16, int64_t ld_slab, int32_t H, const int32_t* masked_m,
+    const int32_t* psum, int32_t E, int32_t align, int32_t max_m,
+    const float* weights, void* out_bf16, int64_t ld_out, int64_t out_rows,
+    void* stream);
+
 /* ---------------------------------------------------------- diagnostics */
 
 /* The fp32 -> e4m3fn conversion every kernel above uses, exposed so it can

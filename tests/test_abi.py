@@ -161,3 +161,33 @@ def test_product_path_never_touches_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+(oracle|"
                                      r"synthetic_inputs)\b", src, re.M), f
+
+
+def test_psum_repack_validation(mxq):
+    L = mxq.lib()
+    assert L.moe_m_indices_from_psum(FAKE, 0, 128, 10, FAKE, None) == INVALID
+    assert L.moe_m_indices_from_psum(FAKE, 4, 0, 10, FAKE, None) == INVALID
+    assert L.moe_m_indices_from_psum(None, 4, 128, 0, None, None) == 0
+    ok = dict(x=FAKE, ld_x=256, rows=64, rb=256, xs=None, xs_rs=0, xs_cs=0,
+              sc=0, se=0, psum=FAKE, E=4, al=128, mm=8, slab=FAKE, ld_s=256,
+              ss=None, ss_rs=0, ss_cs=0, masked=FAKE, flags=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.moe_expand_to_masked_slab(
+            a["x"], a["ld_x"], a["rows"], a["rb"], a["xs"], a["xs_rs"],
+            a["xs_cs"], a["sc"], a["se"], a["psum"], a["E"], a["al"],
+            a["mm"], a["slab"], a["ld_s"], a["ss"], a["ss_rs"], a["ss_cs"],
+            a["masked"], a["flags"], None)
+
+    assert call(rb=100, ld_x=112, ld_s=112) == UNSUPPORTED  # 16-byte rows
+    assert call(ld_s=128) == INVALID            # slab stride below the row
+    assert call(mm=0) == INVALID
+    assert call(flags=None) == INVALID
+    assert call(xs=FAKE, ss=FAKE, sc=7, se=2) == INVALID  # 1- or 4-byte only
+    assert call(xs=FAKE, ss=FAKE, sc=7, se=4, xs_rs=30, xs_cs=4, ss_rs=28,
+                ss_cs=4) == INVALID             # misaligned 4-byte stride
+    assert L.moe_masked_slab_to_expand(FAKE, 64, 60, FAKE, FAKE, 4, 128, 8,
+                                       None, FAKE, 64, 10, None) == INVALID
+    assert L.moe_masked_slab_to_expand(FAKE, 64, 64, FAKE, FAKE, 4, 128, 8,
+                                       None, FAKE, 64, 0, None) == 0

@@ -39,6 +39,13 @@ def test_graph_replay_full_path(ora):
     S_s = torch.empty(1, dtype=torch.float32, device=DEV)
     rws = torch.empty(mxq.requant_workspace_bytes(T, H), dtype=torch.uint8,
                       device=DEV)
+    # psum repack: a 4-expert expanded layout of R rows
+    psum_s = torch.zeros(4, dtype=torch.int32, device=DEV)
+    slab_s = torch.empty((4 * 64, H), dtype=torch.bfloat16, device=DEV)
+    mm_s = torch.empty(4, dtype=torch.int32, device=DEV)
+    fl_s = torch.empty(1, dtype=torch.int32, device=DEV)
+    pm_s = torch.empty(R, dtype=torch.int32, device=DEV)
+    back_s = torch.empty((R, H), dtype=torch.bfloat16, device=DEV)
 
     def step():
         lay = mxq.moe_layout(ids_s, 0, E, "compact", num_rows=R, out=lay_out,
@@ -48,6 +55,15 @@ def test_graph_replay_full_path(ora):
         mxq.mx_quant_live_rows(x_s, 2, live_s, q=qmx_s, scales=smx_s)
         mxq.requant_per_token_to_per_tensor(rq_in, rs_in, q_out=rq_out,
                                             tensor_scale=S_s, workspace=rws)
+        lib = mxq.lib()
+        st = torch.cuda.current_stream().cuda_stream
+        assert lib.moe_expand_to_masked_slab(
+            y_s.data_ptr(), H * 2, R, H * 2, None, 0, 0, 0, 0,
+            psum_s.data_ptr(), 4, 16, 64, slab_s.data_ptr(), H * 2, None, 0,
+            0, mm_s.data_ptr(), fl_s.data_ptr(), st) == 0
+        mxq.moe_masked_slab_to_expand(slab_s, mm_s, psum_s, 64, 16,
+                                      out=back_s)
+        mxq.moe_m_indices_from_psum(psum_s, R, 16, out=pm_s)
 
     say("graph: warm-up on a side stream")
     side = torch.cuda.Stream()
@@ -70,6 +86,9 @@ def test_graph_replay_full_path(ora):
         y = si.gaussian_bf16(rng, (R, H))
         live = np.array([rep * 11 % 48, 48 - rep * 7], np.int32)
         rq, rs = si.per_token_fp8(rng, T, H)
+        counts = [int(c) for c in rng.integers(0, 65, 4)]
+        from test_oracle_psum import build_layout
+        _, psum_h, _, _ = build_layout(counts, 16, 1)
         ids_s.copy_(i32_to_dev(ids))
         x_s.copy_(bf16_to_dev(x))
         w_s.copy_(f32_to_dev(w))
@@ -77,6 +96,8 @@ def test_graph_replay_full_path(ora):
         live_s.copy_(i32_to_dev(live))
         rq_in.copy_(u8_to_dev(rq))
         rs_in.copy_(f32_to_dev(rs))
+        psum_s.copy_(torch.from_numpy(psum_h).to(DEV))
+        back_s.view(torch.int16).fill_(0x1234)
         q_s.fill_(0xA5)
         sc_s.fill_(0xA5)
         qmx_s.fill_(0xA5)
@@ -104,5 +125,17 @@ def test_graph_replay_full_path(ora):
         rq_ref, S_ref = ora.requant_per_token_to_per_tensor(rq, rs)
         assert_equal(host(rq_out), rq_ref, "requant")
         assert np.float32(host(S_s)[0]) == np.float32(S_ref)
+        y8 = y.view(np.uint8).reshape(R, H * 2)
+        ref_slab = np.zeros((4 * 64, H * 2), np.uint8)
+        _, _, mm_ref, fl_ref = ora.expand_to_masked_slab(y8, psum_h, 16, 64,
+                                                         slab=ref_slab)
+        assert_equal(host(mm_s), mm_ref, "psum masked_m")
+        assert int(host(fl_s)[0]) == fl_ref
+        back_ref = ora.masked_slab_to_expand(
+            ref_slab.view(np.uint16), mm_ref, psum_h, 16, 64,
+            out=np.full((R, H), 0x1234, np.uint16))
+        assert_equal(bf16_to_host(back_s), back_ref, "psum round trip")
+        assert_equal(host(pm_s), ora.m_indices_from_psum(psum_h, 16, R),
+                     "psum m_indices")
         # eager work between replays
         _ = (x_s.float() * 2).sum().item()
