@@ -66,6 +66,11 @@ def lib() -> ctypes.CDLL:
             "ora_e4m3_encode_bits_range": (None, [_u32, _i64, _p]),
             "ora_pow2_scale_exponent": (_i32, [ctypes.c_double]),
             "ora_quant_row": (None, [_p, _i32, _i32, _p, _p]),
+            "ora_quant_row_rule": (None, [_p, _i32, _i32, _i32, _p, _p]),
+            "ora_ocp_mx_exponent": (_i32, [ctypes.c_double]),
+            "ora_scatter_quant_ex": (None, [_p, _i64, _i64, _i32, _p, _i32,
+                                            _i32, _i32, _p, _i64, _p, _i64,
+                                            _i64]),
             "ora_compact_row_bound": (_i64, [_i64, _i32, _i32]),
             "ora_should_use_masked": (_i32, [_i32, _i32]),
             "ora_moe_layout": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _i32,
@@ -147,13 +152,20 @@ def pow2_scale_exponent(amax: float) -> int:
     return int(lib().ora_pow2_scale_exponent(float(amax)))
 
 
-def quant_row(x_bf16, G: int):
+RULES = {"ceil": 0, "ocp_floor": 1}
+
+
+def quant_row(x_bf16, G: int, rule: str = "ceil"):
     x = _c(x_bf16, np.uint16)
     H = x.shape[-1]
     q = np.empty(H, np.uint8)
     s = np.empty(H // G, np.uint8)
-    lib().ora_quant_row(_ptr(x), H, G, _ptr(q), _ptr(s))
+    lib().ora_quant_row_rule(_ptr(x), H, G, RULES[rule], _ptr(q), _ptr(s))
     return q, s
+
+
+def ocp_mx_exponent(amax: float) -> int:
+    return int(lib().ora_ocp_mx_exponent(float(amax)))
 
 
 # ------------------------------------------------------------------- layout
@@ -214,6 +226,39 @@ def scatter_quant(x_bf16, src2dst, G: int, num_rows: int, q=None, s=None):
     lib().ora_scatter_quant(_ptr(x), H, T, H, _ptr(d), K, G, _ptr(q),
                             q.shape[1], _ptr(s), s.shape[1])
     return q, s
+
+
+def scatter_quant_ex(x_bf16, src2dst, G: int, num_rows: int, rule="ceil",
+                     scale_layout="rows", q=None, s=None):
+    """scatter_quant with an exponent rule and a scale placement:
+    "rows" = uint8 [num_rows, H/G]; "packed_mn" = uint32 [ceil(H/G/4),
+    align(num_rows, 4)] holding four scale bytes per word, rows contiguous."""
+    x = _c(x_bf16, np.uint16)
+    d = _c(src2dst, np.int32)
+    T, H = x.shape
+    K = d.shape[1]
+    ng = H // G
+    if q is None:
+        q = np.zeros((num_rows, H), np.uint8)
+    if scale_layout == "rows":
+        if s is None:
+            s = np.zeros((num_rows, ng), np.uint8)
+        s_rs, s_c4 = s.shape[1], 4
+    else:
+        ld_mn = -(-num_rows // 4) * 4
+        if s is None:
+            s = np.zeros((-(-ng // 4), ld_mn), np.uint32)
+        s_rs, s_c4 = 4, 4 * s.shape[1]
+    lib().ora_scatter_quant_ex(_ptr(x), H, T, H, _ptr(d), K, G, RULES[rule],
+                               _ptr(q), q.shape[1], _ptr(s), s_rs, s_c4)
+    return q, s
+
+
+def unpack_mn_scales(packed: np.ndarray, rows: int, ng: int) -> np.ndarray:
+    """[ceil(ng/4), ld_mn] uint32 words -> [rows, ng] scale bytes."""
+    b = np.ascontiguousarray(packed).view(np.uint8).reshape(
+        packed.shape[0], packed.shape[1], 4)
+    return np.transpose(b, (1, 0, 2)).reshape(packed.shape[1], -1)[:rows, :ng]
 
 
 def mx_quant_live_rows(x_bf16, num_segments: int, live_counts, G: int = 32,

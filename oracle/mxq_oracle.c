@@ -39,6 +39,9 @@
  *   R7  combine: fp32 accumulator from +0, one fused multiply-add per
  *       assignment in ascending j, non-local assignments skipped, result
  *       rounded to bf16 (nearest, ties to even) or kept as fp32.
+ *   R8  the OCP Microscaling rule, offered beside R2: e = floor(log2 amax) - 8
+ *       (8 = largest exponent of e4m3), clamped to [-127, 127]; payload
+ *       values then reach up to 2^9 and saturate to +-448.
  *
  * Floating-point: built with -ffp-contract=off.  Quantization arithmetic is
  * done in double, where every step is exact (power-of-two scaling of values
@@ -203,21 +206,43 @@ int ora_pow2_scale_exponent(double amax) {
   return e;
 }
 
+/* R8: the OCP Microscaling shared exponent for e4m3 elements, whose largest
+ * exponent is 8: floor(log2 amax) - 8, clamped to [-127, 127]; an all-zero
+ * group gets -127 [P3 Implementation breakdown item 3 and P4 Motivation name
+ * the formats the consumers read; the rule itself is the OCP MX one]. */
+int ora_ocp_mx_exponent(double amax) {
+  if (!(amax > 0.0)) return -127;
+  int E;
+  frexp(amax, &E); /* amax = f * 2^E, f in [0.5, 1): floor(log2 amax) = E-1 */
+  int e = (E - 1) - 8;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
 /* One row of H bf16 values -> H e4m3 bytes and H/G scale bytes (byte = e+127).
- * Each group's payload is x * 2^-e, which is exact in double. */
-void ora_quant_row(const uint16_t* x, int32_t H, int32_t G, uint8_t* q,
-                   uint8_t* s) {
+ * rule 0 = R2 (smallest exponent without clipping), rule 1 = R8 (OCP MX).
+ * Each group's payload is x * 2^-e, which is exact in double; the encoder
+ * saturates what R8 pushes past 448. */
+void ora_quant_row_rule(const uint16_t* x, int32_t H, int32_t G, int32_t rule,
+                        uint8_t* q, uint8_t* s) {
   for (int32_t g = 0; g < H / G; ++g) {
     double amax = 0.0;
     for (int32_t i = g * G; i < (g + 1) * G; ++i) {
       double v = fabs(bf16_to_double(x[i]));
       if (v > amax) amax = v;
     }
-    int e = ora_pow2_scale_exponent(amax);
+    int e = rule == 1 ? ora_ocp_mx_exponent(amax)
+                      : ora_pow2_scale_exponent(amax);
     for (int32_t i = g * G; i < (g + 1) * G; ++i)
       q[i] = ora_e4m3_encode(ldexp(bf16_to_double(x[i]), -e));
     s[g] = (uint8_t)(e + 127);
   }
+}
+
+void ora_quant_row(const uint16_t* x, int32_t H, int32_t G, uint8_t* q,
+                   uint8_t* s) {
+  ora_quant_row_rule(x, H, G, 0, q, s);
 }
 
 /* ------------------------------------------------------------- layout */
@@ -334,6 +359,39 @@ void ora_scatter_quant(const uint16_t* x, int64_t ld_x, int64_t T, int32_t H,
         if (d < 0) continue;
         memcpy(q + d * ld_q, rq, (size_t)H);
         memcpy(s + d * ld_s, rs, (size_t)(H / G));
+      }
+    }
+    free(rq);
+    free(rs);
+  }
+}
+
+/* The same scatter with a choice of exponent rule and of scale placement:
+ * scale byte g of row d goes to byte d*s_rs + (g/4)*s_c4 + g%4.  Row-major
+ * bytes are s_rs = ld_s, s_c4 = 4; the packed layout with four bytes per
+ * 32-bit word and rows contiguous inside each word column (MN-major) is
+ * s_rs = 4, s_c4 = 4 * ld_mn [P3 Implementation breakdown item 3 and Review
+ * highlights item 3: column-major packed UE8M0 scales]. */
+void ora_scatter_quant_ex(const uint16_t* x, int64_t ld_x, int64_t T,
+                          int32_t H, const int32_t* src2dst, int32_t K,
+                          int32_t G, int32_t rule, uint8_t* q, int64_t ld_q,
+                          uint8_t* s, int64_t s_rs, int64_t s_c4) {
+#pragma omp parallel
+  {
+    uint8_t* rq = (uint8_t*)malloc((size_t)H);
+    uint8_t* rs = (uint8_t*)malloc((size_t)(H / G));
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      int any = 0;
+      for (int32_t j = 0; j < K; ++j) any |= src2dst[t * K + j] >= 0;
+      if (!any) continue;
+      ora_quant_row_rule(x + t * ld_x, H, G, rule, rq, rs);
+      for (int32_t j = 0; j < K; ++j) {
+        int64_t d = src2dst[t * K + j];
+        if (d < 0) continue;
+        memcpy(q + d * ld_q, rq, (size_t)H);
+        for (int32_t g = 0; g < H / G; ++g)
+          s[d * s_rs + (g / 4) * s_c4 + g % 4] = rs[g];
       }
     }
     free(rq);
