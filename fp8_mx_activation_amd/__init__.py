@@ -24,7 +24,8 @@ __all__ = [
     "moe_compact_row_bound", "moe_should_use_masked",
     "moe_layout_workspace_bytes", "requant_workspace_bytes",
     "moe_layout", "moe_read_overflow", "moe_scatter_quant",
-    "mx_quant_live_rows", "live_rows_view",
+    "mx_quant_live_rows", "live_rows_view", "SCALE_RULES",
+    "moe_scatter_quant_ex", "mx_quant_live_rows_ex", "packed_mn_scales",
     "requant_per_token_to_per_tensor", "moe_combine", "mxq_e4m3_encode_f32",
     "mxq_abi_version", "moe_m_indices_from_psum", "moe_expand_to_masked_slab",
     "moe_masked_slab_to_expand",
@@ -37,6 +38,8 @@ MXQ_OK = 0
 MXQ_ERR_CAPACITY_OVERFLOW = 3
 LAYOUT_KINDS = {"compact": 0, "masked": 1}
 SCALE_FORMATS = {"ue8m0_g128": (0, 128), "e8m0_g32": (1, 32)}
+SCALE_RULES = {"no_clip": 0, "ocp_floor": 1}
+SCALE_LAYOUTS = ("rows", "packed_mn")
 OUT_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 
 _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, \
@@ -54,6 +57,11 @@ _SIGNATURES = {
                                  _i64, _p, _i64, _i64, _p]),
     "mx_quant_live_rows": (_i32, [_p, _i64, _i32, _i64, _p, _i32, _i32, _p,
                                   _i64, _p, _i64, _p]),
+    "moe_scatter_quant_ex": (_i32, [_p, _i64, _i64, _i32, _p, _i32, _i32,
+                                    _i32, _p, _i64, _p, _i64, _i64, _i64,
+                                    _p]),
+    "mx_quant_live_rows_ex": (_i32, [_p, _i64, _i32, _i64, _p, _i32, _i32,
+                                     _i32, _p, _i64, _p, _i64, _i64, _p]),
     "requant_per_token_to_per_tensor": (_i32, [_p, _i64, _p, _i64, _i32, _p,
                                                _i64, _p, _p, _sz, _p]),
     "moe_combine": (_i32, [_p, _i64, _i64, _p, _p, _i64, _i32, _i32, _p, _i64,
@@ -303,6 +311,102 @@ def mx_quant_live_rows(x: torch.Tensor, num_segments: int,
                                   code, _ptr(qq), ld_q, _ptr(ss), ld_s,
                                   _stream(x))
     _check("mx_quant_live_rows", st)
+    return q, scales
+
+
+def packed_mn_scales(rows: int, groups: int, device) -> torch.Tensor:
+    """Empty packed MN-major scale tensor: int32 ``[ceil(groups/4),
+    align(rows, 4)]``, four scale bytes per word (group g of row r in byte
+    g % 4 of word ``[g // 4, r]``), rows contiguous."""
+    return torch.empty((-(-groups // 4), -(-rows // 4) * 4),
+                       dtype=torch.int32, device=device)
+
+
+def _scale_place(scales: torch.Tensor | None, layout: str, rows: int,
+                 groups: int, device):
+    """(tensor, byte pointer tensor, row stride, quad stride) for a scale
+    placement; allocates the tensor when none is given."""
+    if layout == "rows":
+        if scales is None:
+            scales = torch.empty((rows, groups), dtype=torch.uint8,
+                                 device=device)
+        ss = _u8(scales)
+        ld = _rows(ss, "scales", (torch.uint8,))
+        if ss.shape[0] < rows or ss.shape[1] < groups:
+            raise ValueError("scales must be at least [%d, %d]"
+                             % (rows, groups))
+        return scales, ss, ld, 4
+    if layout != "packed_mn":
+        raise ValueError("scale_layout must be one of %s" % (SCALE_LAYOUTS,))
+    if scales is None:
+        scales = packed_mn_scales(rows, groups, device)
+    if scales.dtype != torch.int32 or scales.dim() != 2 or \
+            scales.shape[0] < -(-groups // 4) or scales.shape[1] < rows or \
+            (scales.shape[0] > 1 and scales.stride(1) != 1):
+        raise ValueError("packed scales must be int32 [ceil(groups/4), >= "
+                         "rows] with rows contiguous")
+    return scales, scales, 4, 4 * scales.stride(0)
+
+
+def moe_scatter_quant_ex(x: torch.Tensor, src2dst: torch.Tensor,
+                         num_rows: int, fmt: str = "ue8m0_g128",
+                         rule: str = "no_clip", scale_layout: str = "rows",
+                         q: torch.Tensor | None = None,
+                         scales: torch.Tensor | None = None):
+    """``moe_scatter_quant`` with an exponent ``rule`` (``"no_clip"`` or
+    ``"ocp_floor"``) and a ``scale_layout``: ``"rows"`` (uint8 [rows,
+    groups]) or ``"packed_mn"`` (see ``packed_mn_scales``)."""
+    _dev(x, "x")
+    code, G = SCALE_FORMATS[fmt]
+    ld_x = _rows(x, "x", (torch.bfloat16,))
+    T, H = x.shape
+    if src2dst.dtype != torch.int32 or src2dst.dim() != 2 or \
+            src2dst.shape[0] != T or not src2dst.is_contiguous():
+        raise ValueError("src2dst must be contiguous int32 [T, K]")
+    K = src2dst.shape[1]
+    if q is None:
+        q = _empty_rows_u8(num_rows, H, x.device)
+    qq = _u8(q)
+    ld_q = _rows(qq, "q", (torch.uint8,))
+    if qq.shape[0] < num_rows:
+        raise ValueError("q has fewer than num_rows rows")
+    scales, sp, rs, c4 = _scale_place(scales, scale_layout, num_rows, H // G,
+                                      x.device)
+    st = lib().moe_scatter_quant_ex(_ptr(x), ld_x, T, H, _ptr(src2dst), K,
+                                    code, SCALE_RULES[rule], _ptr(qq), ld_q,
+                                    _ptr(sp), rs, c4, num_rows, _stream(x))
+    _check("moe_scatter_quant_ex", st)
+    return q, scales
+
+
+def mx_quant_live_rows_ex(x: torch.Tensor, num_segments: int,
+                          live_counts: torch.Tensor, fmt: str = "e8m0_g32",
+                          rule: str = "no_clip", scale_layout: str = "rows",
+                          q: torch.Tensor | None = None,
+                          scales: torch.Tensor | None = None):
+    """``mx_quant_live_rows`` with an exponent rule and scale layout as in
+    ``moe_scatter_quant_ex``."""
+    _dev(x, "x")
+    _dev(live_counts, "live_counts")
+    code, G = SCALE_FORMATS[fmt]
+    ld_x = _rows(x, "x", (torch.bfloat16,))
+    rows, H = x.shape
+    if num_segments <= 0 or rows % num_segments:
+        raise ValueError("rows must split into num_segments equal segments")
+    if live_counts.dtype != torch.int32 or live_counts.numel() != \
+            num_segments or not live_counts.is_contiguous():
+        raise ValueError("live_counts must be contiguous int32 [segments]")
+    if q is None:
+        q = _empty_rows_u8(rows, H, x.device)
+    qq = _u8(q)
+    ld_q = _rows(qq, "q", (torch.uint8,))
+    scales, sp, rs, c4 = _scale_place(scales, scale_layout, rows, H // G,
+                                      x.device)
+    st = lib().mx_quant_live_rows_ex(_ptr(x), ld_x, num_segments,
+                                     rows // num_segments, _ptr(live_counts),
+                                     H, code, SCALE_RULES[rule], _ptr(qq),
+                                     ld_q, _ptr(sp), rs, c4, _stream(x))
+    _check("mx_quant_live_rows_ex", st)
     return q, scales
 
 

@@ -94,6 +94,15 @@ __device__ __forceinline__ int pow2_exponent(uint32_t m) {
   return e > 127 ? 127 : e;
 }
 
+// OCP Microscaling shared exponent for e4m3 elements (largest element
+// exponent 8): floor(log2 amax) - 8, which for a bf16 amax is its exponent
+// field minus 135; zero and subnormals clamp to -127.
+__device__ __forceinline__ int ocp_floor_exponent(uint32_t m) {
+  int e = (int)(m >> 7) - 135;
+  e = e < -127 ? -127 : e;
+  return e > 127 ? 127 : e;
+}
+
 // 2^-e as a float; e in [-127, 126] keeps it a normal number.
 __device__ __forceinline__ float pow2_neg(int e) {
   return __uint_as_float((uint32_t)(127 - e) << 23);
@@ -108,19 +117,36 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c,
   return (uint32_t)w;
 }
 
+// Exponent rules: the smallest exponent that needs no clipping, or the OCP
+// Microscaling floor rule, whose payload can exceed 448 and is clamped to
+// +-448 before conversion (the conversion is only relied on below 464).
+enum ScaleRule { kNoClip = 0, kOcpFloor = 1 };
+
+template <int RULE>
+__device__ __forceinline__ float clip448(float y) {
+  if constexpr (RULE == kOcpFloor)
+    return __builtin_fminf(__builtin_fmaxf(y, -448.0f), 448.0f);
+  return y;
+}
+
 // Eight bf16 (one 16-byte vector) * factor -> eight e4m3 bytes.
+template <int RULE>
 __device__ __forceinline__ void quant8(const u32x4& v, float f, uint32_t& lo,
                                        uint32_t& hi) {
-  lo = pack4_e4m3(bf16_lo(v.x) * f, bf16_hi(v.x) * f, bf16_lo(v.y) * f,
-                  bf16_hi(v.y) * f);
-  hi = pack4_e4m3(bf16_lo(v.z) * f, bf16_hi(v.z) * f, bf16_lo(v.w) * f,
-                  bf16_hi(v.w) * f);
+  lo = pack4_e4m3(clip448<RULE>(bf16_lo(v.x) * f),
+                  clip448<RULE>(bf16_hi(v.x) * f),
+                  clip448<RULE>(bf16_lo(v.y) * f),
+                  clip448<RULE>(bf16_hi(v.y) * f));
+  hi = pack4_e4m3(clip448<RULE>(bf16_lo(v.z) * f),
+                  clip448<RULE>(bf16_hi(v.z) * f),
+                  clip448<RULE>(bf16_lo(v.w) * f),
+                  clip448<RULE>(bf16_hi(v.w) * f));
 }
 
 // Sixteen consecutive bf16 channels held by one lane (two 16-byte vectors)
 // and the lanes of its group (G / 16 lanes): returns the 16 e4m3 bytes and
 // writes the group exponent.  Every lane of a group must be active.
-template <int G>
+template <int G, int RULE = kNoClip>
 __device__ __forceinline__ u32x4 quant16(const u32x4& a, const u32x4& b,
                                          int& e_out) {
   uint32_t m = max(max(bf16x2_absmax_bits(a.x), bf16x2_absmax_bits(a.y)),
@@ -128,13 +154,22 @@ __device__ __forceinline__ u32x4 quant16(const u32x4& a, const u32x4& b,
   m = max(m, max(max(bf16x2_absmax_bits(b.x), bf16x2_absmax_bits(b.y)),
                  max(bf16x2_absmax_bits(b.z), bf16x2_absmax_bits(b.w))));
   m = group_max<G / 16>(m);
-  const int e = pow2_exponent(m);
+  const int e = RULE == kOcpFloor ? ocp_floor_exponent(m) : pow2_exponent(m);
   const float f = pow2_neg(e);
   u32x4 out;
-  quant8(a, f, out.x, out.y);
-  quant8(b, f, out.z, out.w);
+  quant8<RULE>(a, f, out.x, out.y);
+  quant8<RULE>(b, f, out.z, out.w);
   e_out = e;
   return out;
+}
+
+// Byte offset of scale g of a row: row*rs + (g/4)*c4 + g%4.  rs = row
+// stride and c4 = 4 give row-major bytes; rs = 4 and c4 = 4*ld give the
+// packed layout with four bytes per 32-bit word and rows contiguous
+// (MN-major).
+__device__ __forceinline__ int64_t scale_addr(int64_t row, int g, int64_t rs,
+                                              int64_t c4) {
+  return row * rs + (int64_t)(g >> 2) * c4 + (g & 3);
 }
 
 }  // namespace mxq

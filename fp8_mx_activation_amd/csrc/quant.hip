@@ -28,11 +28,12 @@ using namespace mxq;
 // merge in L2.  Destinations come from src2dst (uniform per block: scalar
 // loads); a token without a destination in [0, num_rows) is skipped before
 // its row is read.
-template <int G>
+template <int G, int RULE>
 __global__ __launch_bounds__(1024) void scatter_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, int32_t H,
     const int32_t* __restrict__ src2dst, int32_t K, uint8_t* __restrict__ q,
-    int64_t ld_q, uint8_t* __restrict__ s, int64_t ld_s, int64_t num_rows) {
+    int64_t ld_q, uint8_t* __restrict__ s, int64_t s_rs, int64_t s_c4,
+    int64_t num_rows) {
   extern __shared__ __align__(16) uint8_t row[];  // [H] fp8, then [H/G] scales
   const int64_t t = blockIdx.x;
   const int32_t* dl = src2dst + t * K;
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(1024) void scatter_quant_kernel(
     const u32x4 a = load16(xr + col);
     const u32x4 b = load16(xr + col + 8);
     int e;
-    const u32x4 v = quant16<G>(a, b, e);
+    const u32x4 v = quant16<G, RULE>(a, b, e);
     *reinterpret_cast<u32x4*>(row + col) = v;
     if (lead) row[H + col / G] = (uint8_t)(e + 127);
   }
@@ -62,19 +63,18 @@ __global__ __launch_bounds__(1024) void scatter_quant_kernel(
     uint8_t* qr = q + d * ld_q;
     for (int c = lane * 16; c < H; c += 64 * 16)
       store16_nt(qr + c, *reinterpret_cast<const u32x4*>(row + c));
-    uint8_t* sr = s + d * ld_s;
-    for (int g = lane; g < ng; g += 64) sr[g] = row[H + g];
+    for (int g = lane; g < ng; g += 64) s[scale_addr(d, g, s_rs, s_c4)] = row[H + g];
   }
 }
 
 // Send-side quant.  Segment g owns blocks [g*bps, (g+1)*bps); block i of a
 // segment handles its live rows i, i + bps, ...  The grid depends only on the
 // host arguments; blocks past the live count return at once.
-template <int G>
+template <int G, int RULE>
 __global__ __launch_bounds__(1024) void live_rows_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, int64_t rps, int32_t bps,
     const int32_t* __restrict__ live, int32_t H, uint8_t* __restrict__ q,
-    int64_t ld_q, uint8_t* __restrict__ s, int64_t ld_s) {
+    int64_t ld_q, uint8_t* __restrict__ s, int64_t s_rs, int64_t s_c4) {
   const int32_t g = blockIdx.x / bps;
   const int32_t i = blockIdx.x - g * bps;
   int64_t n = live[g];
@@ -87,9 +87,9 @@ __global__ __launch_bounds__(1024) void live_rows_kernel(
       const u32x4 a = load16(xr + col);
       const u32x4 b = load16(xr + col + 8);
       int e;
-      const u32x4 v = quant16<G>(a, b, e);
+      const u32x4 v = quant16<G, RULE>(a, b, e);
       store16(q + row * ld_q + col, v);
-      if (lead) s[row * ld_s + col / G] = (uint8_t)(e + 127);
+      if (lead) s[scale_addr(row, col / G, s_rs, s_c4)] = (uint8_t)(e + 127);
     }
   }
 }
@@ -119,17 +119,52 @@ bool rows_ok_u8(const void* p, int64_t ld) {
   return aligned16(p) && ld % 16 == 0;
 }
 
+// Scale placement check: row-major bytes (c4 == 4, rs >= groups) or packed
+// words with rows contiguous (rs == 4, c4 >= 4 * rows); both keep every
+// (row, group) at its own byte.
+bool scale_place_ok(int64_t rs, int64_t c4, int64_t groups, int64_t rows) {
+  if (c4 == 4) return rs >= groups;
+  if (rs == 4) return c4 % 4 == 0 && c4 >= 4 * rows;
+  return false;
+}
+
+template <int G>
+void launch_scatter(int rule, unsigned T, int threads, size_t lds,
+                    hipStream_t s, const uint16_t* x, int64_t ld_x, int32_t H,
+                    const int32_t* src2dst, int32_t K, uint8_t* q,
+                    int64_t ld_q, uint8_t* sc, int64_t rs, int64_t c4,
+                    int64_t num_rows) {
+  if (rule == MXQ_RULE_OCP_FLOOR)
+    scatter_quant_kernel<G, kOcpFloor><<<T, threads, lds, s>>>(
+        x, ld_x, H, src2dst, K, q, ld_q, sc, rs, c4, num_rows);
+  else
+    scatter_quant_kernel<G, kNoClip><<<T, threads, lds, s>>>(
+        x, ld_x, H, src2dst, K, q, ld_q, sc, rs, c4, num_rows);
+}
+
+template <int G>
+void launch_live(int rule, unsigned blocks, int threads, hipStream_t s,
+                 const uint16_t* x, int64_t ld_x, int64_t rps, int32_t bps,
+                 const int32_t* live, int32_t H, uint8_t* q, int64_t ld_q,
+                 uint8_t* sc, int64_t rs, int64_t c4) {
+  if (rule == MXQ_RULE_OCP_FLOOR)
+    live_rows_kernel<G, kOcpFloor><<<blocks, threads, 0, s>>>(
+        x, ld_x, rps, bps, live, H, q, ld_q, sc, rs, c4);
+  else
+    live_rows_kernel<G, kNoClip><<<blocks, threads, 0, s>>>(
+        x, ld_x, rps, bps, live, H, q, ld_q, sc, rs, c4);
+}
+
 }  // namespace
 
-extern "C" mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x,
-                                        int64_t T, int32_t H,
-                                        const int32_t* src2dst, int32_t K,
-                                        mxq_scale_fmt fmt, void* q_fp8,
-                                        int64_t ld_q, uint8_t* scales,
-                                        int64_t ld_s, int64_t num_rows,
-                                        void* stream) {
+extern "C" mxq_status moe_scatter_quant_ex(
+    const void* x_bf16, int64_t ld_x, int64_t T, int32_t H,
+    const int32_t* src2dst, int32_t K, mxq_scale_fmt fmt, mxq_scale_rule rule,
+    void* q_fp8, int64_t ld_q, void* scales, int64_t scale_row_stride,
+    int64_t scale_quad_stride, int64_t num_rows, void* stream) {
   const int G = group_of(fmt);
-  if (G == 0) return MXQ_ERR_UNSUPPORTED;
+  if (G == 0 || (rule != MXQ_RULE_NO_CLIP && rule != MXQ_RULE_OCP_FLOOR))
+    return MXQ_ERR_UNSUPPORTED;
   if (T < 0 || T > INT32_MAX || H <= 0 || H % G != 0 || K < 0 ||
       K > MXQ_MAX_TOPK || num_rows < 0 || num_rows > INT32_MAX)
     return MXQ_ERR_INVALID_ARGUMENT;
@@ -139,7 +174,9 @@ extern "C" mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x,
     return MXQ_ERR_INVALID_ARGUMENT;
   if (num_rows > 0 && (q_fp8 == nullptr || scales == nullptr))
     return MXQ_ERR_INVALID_ARGUMENT;
-  if (ld_q < H || ld_s < H / G) return MXQ_ERR_INVALID_ARGUMENT;
+  if (ld_q < H ||
+      !scale_place_ok(scale_row_stride, scale_quad_stride, H / G, num_rows))
+    return MXQ_ERR_INVALID_ARGUMENT;
   if (!rows_ok_bf16(x_bf16, ld_x) || (num_rows > 0 && !rows_ok_u8(q_fp8, ld_q)))
     return MXQ_ERR_INVALID_ARGUMENT;
   if (num_rows == 0) return MXQ_OK;
@@ -151,33 +188,50 @@ extern "C" mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x,
   hipStream_t s = as_stream(stream);
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   uint8_t* q = static_cast<uint8_t*>(q_fp8);
+  uint8_t* sc = static_cast<uint8_t*>(scales);
   if (G == 128)
-    scatter_quant_kernel<128><<<(unsigned)T, threads, lds, s>>>(
-        x, ld_x, H, src2dst, K, q, ld_q, scales, ld_s, num_rows);
+    launch_scatter<128>(rule, (unsigned)T, threads, lds, s, x, ld_x, H,
+                        src2dst, K, q, ld_q, sc, scale_row_stride,
+                        scale_quad_stride, num_rows);
   else
-    scatter_quant_kernel<32><<<(unsigned)T, threads, lds, s>>>(
-        x, ld_x, H, src2dst, K, q, ld_q, scales, ld_s, num_rows);
+    launch_scatter<32>(rule, (unsigned)T, threads, lds, s, x, ld_x, H,
+                       src2dst, K, q, ld_q, sc, scale_row_stride,
+                       scale_quad_stride, num_rows);
   return launch_status();
 }
 
-extern "C" mxq_status mx_quant_live_rows(const void* x_bf16, int64_t ld_x,
-                                         int32_t num_segments,
-                                         int64_t rows_per_segment,
-                                         const int32_t* live_counts, int32_t H,
-                                         mxq_scale_fmt fmt, void* q_fp8,
-                                         int64_t ld_q, uint8_t* scales,
-                                         int64_t ld_s, void* stream) {
+extern "C" mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x,
+                                        int64_t T, int32_t H,
+                                        const int32_t* src2dst, int32_t K,
+                                        mxq_scale_fmt fmt, void* q_fp8,
+                                        int64_t ld_q, uint8_t* scales,
+                                        int64_t ld_s, int64_t num_rows,
+                                        void* stream) {
+  return moe_scatter_quant_ex(x_bf16, ld_x, T, H, src2dst, K, fmt,
+                              MXQ_RULE_NO_CLIP, q_fp8, ld_q, scales, ld_s, 4,
+                              num_rows, stream);
+}
+
+extern "C" mxq_status mx_quant_live_rows_ex(
+    const void* x_bf16, int64_t ld_x, int32_t num_segments,
+    int64_t rows_per_segment, const int32_t* live_counts, int32_t H,
+    mxq_scale_fmt fmt, mxq_scale_rule rule, void* q_fp8, int64_t ld_q,
+    void* scales, int64_t scale_row_stride, int64_t scale_quad_stride,
+    void* stream) {
   const int G = group_of(fmt);
-  if (G == 0) return MXQ_ERR_UNSUPPORTED;
+  if (G == 0 || (rule != MXQ_RULE_NO_CLIP && rule != MXQ_RULE_OCP_FLOOR))
+    return MXQ_ERR_UNSUPPORTED;
   if (num_segments < 0 || rows_per_segment < 0 || H <= 0 || H % G != 0)
     return MXQ_ERR_INVALID_ARGUMENT;
   if (num_segments == 0 || rows_per_segment == 0) return MXQ_OK;
-  if ((int64_t)num_segments * rows_per_segment > INT32_MAX)
-    return MXQ_ERR_INVALID_ARGUMENT;
+  const int64_t rows = (int64_t)num_segments * rows_per_segment;
+  if (rows > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
   if (x_bf16 == nullptr || live_counts == nullptr || q_fp8 == nullptr ||
       scales == nullptr)
     return MXQ_ERR_INVALID_ARGUMENT;
-  if (ld_x < H || ld_q < H || ld_s < H / G) return MXQ_ERR_INVALID_ARGUMENT;
+  if (ld_x < H || ld_q < H ||
+      !scale_place_ok(scale_row_stride, scale_quad_stride, H / G, rows))
+    return MXQ_ERR_INVALID_ARGUMENT;
   if (!rows_ok_bf16(x_bf16, ld_x) || !rows_ok_u8(q_fp8, ld_q))
     return MXQ_ERR_INVALID_ARGUMENT;
 
@@ -191,15 +245,28 @@ extern "C" mxq_status mx_quant_live_rows(const void* x_bf16, int64_t ld_x,
   hipStream_t s = as_stream(stream);
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   uint8_t* q = static_cast<uint8_t*>(q_fp8);
+  uint8_t* sc = static_cast<uint8_t*>(scales);
   if (G == 32)
-    live_rows_kernel<32><<<(unsigned)blocks, threads, 0, s>>>(
-        x, ld_x, rows_per_segment, (int32_t)bps, live_counts, H, q, ld_q,
-        scales, ld_s);
+    launch_live<32>(rule, (unsigned)blocks, threads, s, x, ld_x,
+                    rows_per_segment, (int32_t)bps, live_counts, H, q, ld_q,
+                    sc, scale_row_stride, scale_quad_stride);
   else
-    live_rows_kernel<128><<<(unsigned)blocks, threads, 0, s>>>(
-        x, ld_x, rows_per_segment, (int32_t)bps, live_counts, H, q, ld_q,
-        scales, ld_s);
+    launch_live<128>(rule, (unsigned)blocks, threads, s, x, ld_x,
+                     rows_per_segment, (int32_t)bps, live_counts, H, q, ld_q,
+                     sc, scale_row_stride, scale_quad_stride);
   return launch_status();
+}
+
+extern "C" mxq_status mx_quant_live_rows(const void* x_bf16, int64_t ld_x,
+                                         int32_t num_segments,
+                                         int64_t rows_per_segment,
+                                         const int32_t* live_counts, int32_t H,
+                                         mxq_scale_fmt fmt, void* q_fp8,
+                                         int64_t ld_q, uint8_t* scales,
+                                         int64_t ld_s, void* stream) {
+  return mx_quant_live_rows_ex(x_bf16, ld_x, num_segments, rows_per_segment,
+                               live_counts, H, fmt, MXQ_RULE_NO_CLIP, q_fp8,
+                               ld_q, scales, ld_s, 4, stream);
 }
 
 extern "C" mxq_status mxq_e4m3_encode_f32(const float* in, int64_t n,

@@ -73,6 +73,13 @@ typedef enum {
   MXQ_SCALE_E8M0_G32 = 1    /* 32 channels per scale  [P4 impl. item 1] */
 } mxq_scale_fmt;
 
+/* Exponent rule for the *_ex quantizers.  MXQ_RULE_NO_CLIP is the rule
+ * above.  MXQ_RULE_OCP_FLOOR is the OCP Microscaling shared exponent
+ * floor(log2 amax) - 8 (8 = largest e4m3 exponent), clamped to [-127, 127]:
+ * payload values then reach up to 2^9 and are clamped to +-448 before
+ * conversion. */
+typedef enum { MXQ_RULE_NO_CLIP = 0, MXQ_RULE_OCP_FLOOR = 1 } mxq_scale_rule;
+
 typedef enum { MXQ_OUT_BF16 = 0, MXQ_OUT_F32 = 1 } mxq_out_dtype;
 
 /* ------------------------------------------------------------ host-only */
@@ -167,6 +174,25 @@ mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x, int64_t T,
                              uint8_t* scales, int64_t ld_s, int64_t num_rows,
                              void* stream);
 
+/* moe_scatter_quant with a choice of exponent rule and of scale placement
+ * [P3 impl. item 3 and Review highlights item 3: consumers read scales
+ * column-major with four UE8M0 bytes packed per 32-bit word].  Scale byte g
+ * of row d is written to scales + d*scale_row_stride +
+ * (g/4)*scale_quad_stride + g%4.  Two placements are accepted:
+ *   row-major bytes:  scale_quad_stride = 4, scale_row_stride >= H/G;
+ *   packed MN-major:  scale_row_stride = 4, scale_quad_stride a multiple of
+ *                     4 and >= 4*num_rows (int32 [ceil(H/G/4), ld], rows
+ *                     contiguous, ld = scale_quad_stride / 4).
+ * moe_scatter_quant(..., ld_s, ...) is this call with MXQ_RULE_NO_CLIP,
+ * scale_row_stride = ld_s and scale_quad_stride = 4. */
+mxq_status moe_scatter_quant_ex(const void* x_bf16, int64_t ld_x, int64_t T,
+                                int32_t H, const int32_t* src2dst, int32_t K,
+                                mxq_scale_fmt fmt, mxq_scale_rule rule,
+                                void* q_fp8, int64_t ld_q, void* scales,
+                                int64_t scale_row_stride,
+                                int64_t scale_quad_stride, int64_t num_rows,
+                                void* stream);
+
 /* Send-side quant over live rows only [P4 Features & motivation and impl.
  * item 1: quantize on the sender over the live tokens, not the padded
  * receive buffer; 224 one-byte scales per 7168-wide row].
@@ -183,6 +209,17 @@ mxq_status mx_quant_live_rows(const void* x_bf16, int64_t ld_x,
                               const int32_t* live_counts, int32_t H,
                               mxq_scale_fmt fmt, void* q_fp8, int64_t ld_q,
                               uint8_t* scales, int64_t ld_s, void* stream);
+
+/* mx_quant_live_rows with an exponent rule and a scale placement, as in
+ * moe_scatter_quant_ex (the packed placement needs scale_quad_stride >= 4 *
+ * num_segments * rows_per_segment). */
+mxq_status mx_quant_live_rows_ex(const void* x_bf16, int64_t ld_x,
+                                 int32_t num_segments, int64_t rows_per_segment,
+                                 const int32_t* live_counts, int32_t H,
+                                 mxq_scale_fmt fmt, mxq_scale_rule rule,
+                                 void* q_fp8, int64_t ld_q, void* scales,
+                                 int64_t scale_row_stride,
+                                 int64_t scale_quad_stride, void* stream);
 
 /* ------------------------------------------------------------- requant */
 

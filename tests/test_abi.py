@@ -104,6 +104,41 @@ def test_scatter_quant_validation(mxq):
     assert call(rows=0, q=None, s=None) == 0
 
 
+def test_scatter_quant_ex_validation(mxq):
+    """Rule and scale placement checks of the variant entry points."""
+    L = mxq.lib()
+    ok = dict(x=FAKE, ld_x=256, T=4, H=640, s2d=FAKE, K=2, fmt=1, rule=0,
+              q=FAKE, ld_q=640, s=FAKE, rs=20, c4=4, rows=18)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        a["ld_x"] = max(a["ld_x"], a["H"])
+        return L.moe_scatter_quant_ex(a["x"], a["ld_x"], a["T"], a["H"],
+                                      a["s2d"], a["K"], a["fmt"], a["rule"],
+                                      a["q"], a["ld_q"], a["s"], a["rs"],
+                                      a["c4"], a["rows"], None)
+
+    def live(**kw):
+        a = dict(ok, **kw)
+        a["ld_x"] = max(a["ld_x"], a["H"])
+        return L.mx_quant_live_rows_ex(a["x"], a["ld_x"], 3, 6, FAKE, a["H"],
+                                       a["fmt"], a["rule"], a["q"],
+                                       a["ld_q"], a["s"], a["rs"], a["c4"],
+                                       None)
+
+    for f in (call, live):
+        assert f(rule=2) == UNSUPPORTED
+        assert f(rule=-1) == UNSUPPORTED
+        assert f(rs=19) == INVALID            # 20 groups need rs >= 20
+        assert f(rs=20, c4=8) == INVALID      # neither placement
+        assert f(rs=4, c4=4 * 18 - 4) == INVALID  # packed: c4 < 4 * rows
+        assert f(rs=4, c4=4 * 18 + 2) == INVALID  # packed: c4 not words
+    # 20 groups of 32: packed needs 5 words per row
+    assert call(T=0, rs=4, c4=4 * 20) == 0
+    assert call(T=0, rule=1) == 0
+    assert call(rows=0, q=None, s=None, rs=4, c4=0) == 0
+
+
 def test_layout_validation(mxq):
     L = mxq.lib()
 
