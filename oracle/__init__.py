@@ -92,6 +92,13 @@ def lib() -> ctypes.CDLL:
             "ora_masked_slab_to_expand": (
                 None, [_p, _i64, _i32, _p, _p, _i32, _i32, _i32, _p, _p, _i64,
                        _i64]),
+            "ora_bf16_round_f64": (ctypes.c_uint16, [ctypes.c_double]),
+            "ora_bf16_round_f64_array": (None, [_p, _i64, _p]),
+            "ora_upscale_fp8": (None, [_p, _i64, _p, _i64, _i64, _i64, _i32,
+                                       _i32, _p, _i64]),
+            "ora_requant_weight_block_ue8m0": (
+                None, [_p, _i64, _i64, _p, _i64, _i64, _i32, _i32, _i32, _i32,
+                       _i32, _p, _p, _i64, _i64]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -145,6 +152,14 @@ def bf16_round(x) -> np.ndarray:
     x = _c(x, np.float32)
     out = np.empty(x.shape, np.uint16)
     lib().ora_bf16_round_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def bf16_round_f64(x) -> np.ndarray:
+    """Round float64 values to bf16 bits once (nearest-even; NaN -> 0x7FC0)."""
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().ora_bf16_round_f64_array(_ptr(x), x.size, _ptr(out))
     return out
 
 
@@ -384,3 +399,53 @@ def masked_slab_to_expand(slab_bf16: np.ndarray, masked_m, psum, align: int,
                                     align, max_m, 0 if w is None else _ptr(w),
                                     _ptr(out), out.shape[1], out.shape[0])
     return out
+
+
+# -------------------------------------------------------- receive-side upscale
+
+def upscale_fp8(q, scales, num_rows: int | None = None, G: int = 128,
+                scales_col_major: bool = False, out=None):
+    """fp8 payload [rows, H] + fp32 group scales -> bf16 bits [rows, H] for
+    the first ``num_rows`` rows.  Scales are [rows, H/G] or, with
+    ``scales_col_major``, [H/G, rows].  ``out`` rows at or past ``num_rows``
+    are left as they are."""
+    qq = _c(q, np.uint8)
+    rows, H = qq.shape
+    n = rows if num_rows is None else num_rows
+    sc = _c(scales, np.float32)
+    if scales_col_major:
+        s_rs, s_cs = 1, sc.shape[1]
+    else:
+        s_rs, s_cs = sc.shape[1], 1
+    if out is None:
+        out = np.zeros((rows, H), np.uint16)
+    assert out.flags.c_contiguous and out.dtype == np.uint16
+    lib().ora_upscale_fp8(_ptr(qq), H, _ptr(sc), s_rs, s_cs, n, H, G,
+                          _ptr(out), out.shape[1])
+    return out
+
+
+# --------------------------------------------------- weight-side requant
+
+def requant_weight_block_ue8m0(q, s_inv, block=(128, 128)):
+    """q: e4m3 bytes [B, N, K] (or [N, K]); s_inv: fp32 [B, ceil(N/bn),
+    ceil(K/bk)].  Returns (q_out bytes, UE8M0 scale bytes [B, nbn, nbk])."""
+    qq = _c(q, np.uint8)
+    squeeze = qq.ndim == 2
+    if squeeze:
+        qq = qq[None]
+    si = _c(s_inv, np.float32)
+    if si.ndim == 2:
+        si = si[None]
+    B, N, K = qq.shape
+    bn, bk = block
+    nbn, nbk = -(-N // bn), -(-K // bk)
+    assert si.shape == (B, nbn, nbk), si.shape
+    q_out = np.empty_like(qq)
+    s_out = np.empty((B, nbn, nbk), np.uint8)
+    lib().ora_requant_weight_block_ue8m0(
+        _ptr(qq), K, N * K, _ptr(si), nbk, nbn * nbk, B, N, K, bn, bk,
+        _ptr(q_out), _ptr(s_out), nbk, nbn * nbk)
+    if squeeze:
+        return q_out[0], s_out[0]
+    return q_out, s_out

@@ -42,6 +42,14 @@
  *   R8  the OCP Microscaling rule, offered beside R2: e = floor(log2 amax) - 8
  *       (8 = largest exponent of e4m3), clamped to [-127, 127]; payload
  *       values then reach up to 2^9 and saturate to +-448.
+ *   R9  receive-side upscale: out = bf16(dec(q) * s) with the product taken
+ *       exactly and rounded once (nearest, ties to even; overflow to inf);
+ *       a NaN result is written as 0x7FC0.  Only the first num_local_tokens
+ *       rows are written.
+ *   R10 weight-side UE8M0 block requant: each [bn, bk] block (128 x 128) is
+ *       dequantized to bf16 with R9's rounding using its fp32 inverse scale,
+ *       then quantized again with R2 over the whole block, the exponent
+ *       stored as one UE8M0 byte per block.  Inputs are finite.
  *
  * Floating-point: built with -ffp-contract=off.  Quantization arithmetic is
  * done in double, where every step is exact (power-of-two scaling of values
@@ -168,6 +176,39 @@ uint16_t ora_bf16_round(float x) {
 
 void ora_bf16_round_array(const float* x, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = ora_bf16_round(x[i]);
+}
+
+/* Round a real number (held exactly in a double) to bf16 once: nearest, ties
+ * to even, overflow to infinity; NaN gives 0x7FC0 (R9).  The bf16 grid
+ * spacing at |x| is 2^-133 below 2^-126 (subnormals) and 2^(floor(log2|x|) -
+ * 7) above it; |x| / spacing is exact, as in the e4m3 encoder. */
+uint16_t ora_bf16_round_f64(double x) {
+  if (isnan(x)) return 0x7FC0;
+  uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  if (a >= ldexp(1.0, 128)) return sign | 0x7F80;
+  int E;
+  frexp(a, &E); /* floor(log2 a) = E - 1 */
+  double spacing = (E - 1 < -126) ? ldexp(1.0, -133) : ldexp(1.0, E - 1 - 7);
+  double n = a / spacing;
+  double lo = floor(n);
+  double frac = n - lo;
+  double r;
+  if (frac > 0.5)
+    r = lo + 1.0;
+  else if (frac < 0.5)
+    r = lo;
+  else
+    r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0;
+  float v = (float)(r * spacing); /* a bf16 value (or 2^128 -> inf): exact */
+  uint32_t w;
+  memcpy(&w, &v, sizeof w);
+  return sign | (uint16_t)((w >> 16) & 0x7FFF);
+}
+
+void ora_bf16_round_f64_array(const double* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ora_bf16_round_f64(x[i]);
 }
 
 void ora_e4m3_encode_array_f32(const float* y, int64_t n, uint8_t* out) {
@@ -584,5 +625,71 @@ void ora_masked_slab_to_expand(const uint16_t* slab, int64_t ld_slab,
         }
       }
     }
+  }
+}
+
+/* ------------------------------------------------------ receive-side upscale */
+
+/* fp8 payload with group-G fp32 scales -> bf16, over the first `rows` rows
+ * [P4 Implementation breakdown item 3 and the aiter.py snippet: an fp8
+ * dispatch carries group-128 fp32 scales, and the receiver turns it back into
+ * bf16 for the first num_local_tokens rows before a kernel that wants bf16].
+ * Scale of (r, channel h) at scales[r * s_rs + (h / G) * s_cs] (R9). */
+void ora_upscale_fp8(const uint8_t* q, int64_t ld_q, const float* scales,
+                     int64_t s_rs, int64_t s_cs, int64_t rows, int32_t H,
+                     int32_t G, uint16_t* out, int64_t ld_out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int32_t h = 0; h < H; ++h) {
+      double s = (double)scales[r * s_rs + (int64_t)(h / G) * s_cs];
+      out[r * ld_out + h] = ora_bf16_round_f64(ora_e4m3_decode(q[r * ld_q + h]) * s);
+    }
+}
+
+/* ------------------------------------------------ weight-side block requant */
+
+/* UE8M0 block requant of block-scaled fp8 weights (R10) [P1 Implementation
+ * breakdown item 1 and the fp8.py snippet: the gate/up and down expert
+ * weights of a standard MoE layer are requantized to UE8M0 block scales at
+ * load time, with bf16 as the dequantized type].  B matrices of [N, K] e4m3
+ * (row stride ld, matrix stride q_bs); inverse scales s_inv [B, ceil(N/bn),
+ * ceil(K/bk)] fp32 (row stride s_ld, matrix stride s_bs): weight = dec(q) *
+ * s_inv of its block.  Writes q_out (same strides as q; may be q itself) and
+ * one scale byte per block to s_out (row stride o_ld, matrix stride o_bs). */
+void ora_requant_weight_block_ue8m0(const uint8_t* q, int64_t ld, int64_t q_bs,
+                                    const float* s_inv, int64_t s_ld,
+                                    int64_t s_bs, int32_t B, int32_t N,
+                                    int32_t K, int32_t bn, int32_t bk,
+                                    uint8_t* q_out, uint8_t* s_out,
+                                    int64_t o_ld, int64_t o_bs) {
+  const int32_t nbn = (N + bn - 1) / bn, nbk = (K + bk - 1) / bk;
+#pragma omp parallel
+  {
+    uint16_t* w = (uint16_t*)malloc((size_t)bn * (size_t)bk * sizeof(uint16_t));
+#pragma omp for collapse(3) schedule(static)
+    for (int32_t b = 0; b < B; ++b)
+      for (int32_t i = 0; i < nbn; ++i)
+        for (int32_t j = 0; j < nbk; ++j) {
+          const int32_t r0 = i * bn, c0 = j * bk;
+          const int32_t nr = (N - r0 < bn) ? N - r0 : bn;
+          const int32_t nc = (K - c0 < bk) ? K - c0 : bk;
+          const double si = (double)s_inv[b * s_bs + (int64_t)i * s_ld + j];
+          double amax = 0.0;
+          for (int32_t r = 0; r < nr; ++r)
+            for (int32_t c = 0; c < nc; ++c) {
+              const uint8_t v = q[b * q_bs + (int64_t)(r0 + r) * ld + c0 + c];
+              const uint16_t h = ora_bf16_round_f64(ora_e4m3_decode(v) * si);
+              w[r * bk + c] = h;
+              const double m = fabs(bf16_to_double(h));
+              if (m > amax) amax = m;
+            }
+          const int e = ora_pow2_scale_exponent(amax);
+          for (int32_t r = 0; r < nr; ++r)
+            for (int32_t c = 0; c < nc; ++c)
+              q_out[b * q_bs + (int64_t)(r0 + r) * ld + c0 + c] =
+                  ora_e4m3_encode(ldexp(bf16_to_double(w[r * bk + c]), -e));
+          s_out[b * o_bs + (int64_t)i * o_ld + j] = (uint8_t)(e + 127);
+        }
+    free(w);
   }
 }
