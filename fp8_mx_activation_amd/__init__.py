@@ -28,7 +28,8 @@ __all__ = [
     "moe_scatter_quant_ex", "mx_quant_live_rows_ex", "packed_mn_scales",
     "requant_per_token_to_per_tensor", "moe_combine", "mxq_e4m3_encode_f32",
     "mxq_abi_version", "moe_m_indices_from_psum", "moe_expand_to_masked_slab",
-    "moe_masked_slab_to_expand",
+    "moe_masked_slab_to_expand", "upscale_fp8_to_bf16",
+    "requant_weight_block_ue8m0",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +74,11 @@ _SIGNATURES = {
                                          _i64, _p, _i64, _i64, _p, _p, _p]),
     "moe_masked_slab_to_expand": (_i32, [_p, _i64, _i32, _p, _p, _i32, _i32,
                                          _i32, _p, _p, _i64, _i64, _p]),
+    "upscale_fp8_to_bf16": (_i32, [_p, _i64, _p, _i64, _i64, _i64, _i32,
+                                   _i32, _p, _i64, _p]),
+    "requant_weight_block_ue8m0": (_i32, [_p, _i64, _i64, _p, _i64, _i64,
+                                          _i32, _i32, _i32, _i32, _i32, _p,
+                                          _p, _i64, _i64, _p]),
     "mxq_status_string": (ctypes.c_char_p, [_i32]),
     "mxq_abi_version": (_i32, []),
 }
@@ -595,3 +601,92 @@ def moe_masked_slab_to_expand(slab: torch.Tensor, masked_m: torch.Tensor,
         max_m, _ptr(weights), _ptr(out), ld_out, out.shape[0], _stream(slab))
     _check("moe_masked_slab_to_expand", st)
     return out
+
+
+# ---------------------------------------------------- receive-side upscale
+
+def upscale_fp8_to_bf16(q: torch.Tensor, scales: torch.Tensor,
+                        num_rows: int | None = None, group: int = 128,
+                        scales_col_major: bool = False,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp8 rows + fp32 group scales -> bf16 rows for the first ``num_rows``
+    rows.  ``scales`` is [rows, H/group], or [H/group, rows] with
+    ``scales_col_major``.  Rows of ``out`` at or past ``num_rows`` keep
+    their contents."""
+    _dev(q, "q")
+    _dev(scales, "scales")
+    qq = _u8(q)
+    ld_q = _rows(qq, "q", (torch.uint8,))
+    rows, H = qq.shape
+    n = rows if num_rows is None else int(num_rows)
+    if not 0 <= n <= rows:
+        raise ValueError("num_rows out of range")
+    if scales.dtype != torch.float32 or scales.dim() != 2:
+        raise TypeError("scales must be fp32 2-D")
+    ng = H // group if group else 0
+    if scales_col_major:
+        if scales.shape[0] < ng or scales.shape[1] < n or \
+                (scales.shape[0] > 1 and scales.stride(1) != 1):
+            raise ValueError("column-major scales must be [H/group, >= rows]")
+        s_rs, s_cs = 1, scales.stride(0)
+    else:
+        if scales.shape[0] < n or scales.shape[1] < ng or \
+                (scales.shape[1] > 1 and scales.stride(1) != 1):
+            raise ValueError("scales must be [>= rows, H/group]")
+        s_rs, s_cs = scales.stride(0), 1
+    if out is None:
+        out = torch.empty((rows, H), dtype=torch.bfloat16, device=q.device)
+    ld_o = _rows(out, "out", (torch.bfloat16,))
+    st = lib().upscale_fp8_to_bf16(_ptr(qq), ld_q, _ptr(scales), s_rs, s_cs,
+                                   n, H, group, _ptr(out), ld_o, _stream(q))
+    _check("upscale_fp8_to_bf16", st)
+    return out
+
+
+# --------------------------------------------------- weight-side requant
+
+def requant_weight_block_ue8m0(q: torch.Tensor, s_inv: torch.Tensor,
+                               block=(128, 128), q_out: torch.Tensor | None =
+                               None, scales_out: torch.Tensor | None = None,
+                               inplace: bool = False):
+    """Block-scaled fp8 weights [B, N, K] (or [N, K]) with fp32 inverse
+    scales [B, ceil(N/128), ceil(K/128)] -> (fp8 weights, UE8M0 scale bytes
+    [B, nbn, nbk]).  ``inplace`` writes the weights over ``q``."""
+    _dev(q, "q")
+    _dev(s_inv, "s_inv")
+    qq = _u8(q)
+    squeeze = qq.dim() == 2
+    q3 = qq.unsqueeze(0) if squeeze else qq
+    s3 = s_inv.unsqueeze(0) if s_inv.dim() == 2 else s_inv
+    if q3.dim() != 3 or not q3.is_contiguous():
+        raise ValueError("q must be contiguous [B, N, K] or [N, K]")
+    if s3.dtype != torch.float32 or s3.dim() != 3 or not s3.is_contiguous():
+        raise ValueError("s_inv must be contiguous fp32 [B, nbn, nbk]")
+    B, N, K = q3.shape
+    bn, bk = block
+    nbn, nbk = -(-N // bn) if bn else 0, -(-K // bk) if bk else 0
+    if tuple(s3.shape) != (B, nbn, nbk):
+        raise ValueError("s_inv must be [%d, %d, %d]" % (B, nbn, nbk))
+    if inplace:
+        qo = q3
+    elif q_out is None:
+        qo = torch.empty_like(q3)
+    else:
+        qo = _u8(q_out)
+        qo = qo.unsqueeze(0) if qo.dim() == 2 else qo
+        if tuple(qo.shape) != (B, N, K) or not qo.is_contiguous():
+            raise ValueError("q_out must match q")
+    if scales_out is None:
+        so = torch.empty((B, nbn, nbk), dtype=torch.uint8, device=q.device)
+    else:
+        so = _u8(scales_out)
+        so = so.unsqueeze(0) if so.dim() == 2 else so
+        if tuple(so.shape) != (B, nbn, nbk) or not so.is_contiguous():
+            raise ValueError("scales_out must be [%d, %d, %d]" % (B, nbn, nbk))
+    st = lib().requant_weight_block_ue8m0(
+        _ptr(q3), K, N * K, _ptr(s3), nbk, nbn * nbk, B, N, K, bn, bk,
+        _ptr(qo), _ptr(so), nbk, nbn * nbk, _stream(q))
+    _check("requant_weight_block_ue8m0", st)
+    if squeeze:
+        return qo[0], so[0]
+    return qo, so

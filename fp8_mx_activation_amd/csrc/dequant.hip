@@ -1,0 +1,239 @@
+// Receive-side upscale (fp8 + group fp32 scales -> bf16) and weight-side
+// UE8M0 block requant (block-scaled fp8 weights -> bf16 -> fp8 with one
+// power-of-two scale per 128 x 128 block).
+//
+// Both round the product of an e4m3 value and an fp32 scale to bf16 exactly
+// once.  That product needs up to 28 significant bits, so the fp32 product
+// alone could land on a bf16 rounding midpoint that the exact product is not
+// on.  mul_round_bf16 keeps the fp32 product's rounding error (one fmaf,
+// exact when the scale is at least 2^-90), folds it in as a sticky bit (round
+// to odd) and then rounds to bf16 with nearest-even; smaller scales take an
+// exact double-precision path, chosen once per scale.
+//
+//   upscale_kernel         one block per row, one lane per 16 bytes (16
+//                          channels) of the row: a 16-byte load, one scale per
+//                          lane, two 16-byte stores.  HBM-bound: 3 bytes per
+//                          channel plus the scales.
+//   weight_requant_kernel  one 256-thread block per 128 x 128 block: each
+//                          thread loads four 16-byte chunks (8 rows of 128 B
+//                          per wavefront instruction), dequantizes them to
+//                          bf16 in registers, the block reduces the largest
+//                          magnitude, and the same threads requantize and
+//                          store.  All reads precede the reduction barrier, so
+//                          the output may be the input itself.
+#include "mxq_device.hpp"
+#include "mxq_host.hpp"
+
+namespace {
+
+using namespace mxq;
+
+// bf16 bits (low 16 bits) of x, given its fp32 rounding p and the exact
+// remainder err = x - p: round to odd (truncate toward zero and set the last
+// bit when inexact), then to bf16 with nearest-even.  Rounding to odd first
+// keeps the second rounding exact, since bf16 drops 16 bits.  NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t round_bf16_sticky(float p, float err) {
+  uint32_t pb = __float_as_uint(p);
+  const uint32_t odd = (pb - ((__float_as_uint(err) ^ pb) >> 31)) | 1u;
+  pb = err != 0.0f ? odd : pb;
+  const uint32_t r = (pb + 0x7FFFu + ((pb >> 16) & 1u)) >> 16;
+  return p != p ? 0x7FC0u : r;
+}
+
+// Exactly rounded a * b for an e4m3 value a and a scale |b| >= 2^-90: every
+// nonzero product is then at least 2^-99, where the fmaf remainder is exact
+// (no underflow), and a zero product has a zero remainder.
+__device__ __forceinline__ uint32_t mul_round_bf16(float a, float b) {
+  const float p = a * b;
+  return round_bf16_sticky(p, __builtin_fmaf(a, b, -p));
+}
+
+// The same for any scale, through an exact double product (4 + 24
+// significant bits) whose fp32 rounding is corrected to odd by comparison.
+__device__ __forceinline__ uint32_t mul_round_bf16_small(float a, float b) {
+  const double x = (double)a * (double)b;
+  const float f = (float)x;
+  uint32_t fb = __float_as_uint(f);
+  const double fd = (double)f;
+  if (fd != x) {
+    if (__builtin_fabs(fd) > __builtin_fabs(x)) fb -= 1u;
+    fb |= 1u;
+  }
+  const uint32_t r = (fb + 0x7FFFu + ((fb >> 16) & 1u)) >> 16;
+  return x != x ? 0x7FC0u : r;
+}
+
+__device__ __forceinline__ bool fast_scale(float b) {
+  return !(__builtin_fabsf(b) < 0x1p-90f);  // NaN takes the fast path too
+}
+
+// Sixteen e4m3 bytes times b -> sixteen bf16 (o0: channels 0-7, o1: 8-15).
+__device__ __forceinline__ void upscale16(const u32x4& v, float b, u32x4& o0,
+                                          u32x4& o1) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r[8];
+  if (fast_scale(b)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+      const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+      r[2 * k] = mul_round_bf16(f01[0], b) | (mul_round_bf16(f01[1], b) << 16);
+      r[2 * k + 1] =
+          mul_round_bf16(f23[0], b) | (mul_round_bf16(f23[1], b) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+      const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+      r[2 * k] = mul_round_bf16_small(f01[0], b) |
+                 (mul_round_bf16_small(f01[1], b) << 16);
+      r[2 * k + 1] = mul_round_bf16_small(f23[0], b) |
+                     (mul_round_bf16_small(f23[1], b) << 16);
+    }
+  }
+  o0 = u32x4{r[0], r[1], r[2], r[3]};
+  o1 = u32x4{r[4], r[5], r[6], r[7]};
+}
+
+template <int G>
+__global__ __launch_bounds__(1024) void upscale_kernel(
+    const uint8_t* __restrict__ q, int64_t ld_q, const float* __restrict__ s,
+    int64_t s_rs, int64_t s_cs, int32_t H, uint16_t* __restrict__ out,
+    int64_t ld_out) {
+  const int64_t r = blockIdx.x;
+  const uint8_t* qr = q + r * ld_q;
+  const float* sr = s + r * s_rs;
+  uint16_t* orow = out + r * ld_out;
+  for (int32_t col = threadIdx.x * 16; col < H; col += blockDim.x * 16) {
+    const u32x4 v = load16(qr + col);
+    const float b = sr[(int64_t)(col / G) * s_cs];
+    u32x4 o0, o1;
+    upscale16(v, b, o0, o1);
+    store16(orow + col, o0);
+    store16(orow + col + 8, o1);
+  }
+}
+
+constexpr int kWBlock = 128;
+constexpr int kWThreads = 256;
+constexpr int kWChunks = kWBlock * kWBlock / 16 / kWThreads;  // 4 per thread
+
+__global__ __launch_bounds__(kWThreads) void weight_requant_kernel(
+    const uint8_t* q, int64_t ld, int64_t q_bs, const float* __restrict__ s_inv,
+    int64_t s_ld, int64_t s_bs, int32_t N, int32_t K, int32_t nbn,
+    int32_t nbk, uint8_t* q_out, uint8_t* __restrict__ s_out, int64_t o_ld,
+    int64_t o_bs) {
+  __shared__ uint32_t wmax[kWThreads / 64];
+  const int64_t blk = blockIdx.x;
+  const int32_t j = (int32_t)(blk % nbk);
+  const int64_t t = blk / nbk;
+  const int32_t i = (int32_t)(t % nbn);
+  const int64_t b = t / nbn;
+  const float si = s_inv[b * s_bs + (int64_t)i * s_ld + j];
+  const int32_t r0 = i * kWBlock, c0 = j * kWBlock;
+  const uint8_t* qb = q + b * q_bs;
+
+  u32x4 w0[kWChunks], w1[kWChunks];  // 16 bf16 per chunk
+  uint32_t m = 0;
+#pragma unroll
+  for (int u = 0; u < kWChunks; ++u) {
+    const int k = threadIdx.x + u * kWThreads;
+    const int32_t rr = r0 + (k >> 3), cc = c0 + (k & 7) * 16;
+    if (rr < N && cc < K) {
+      const u32x4 v = load16(qb + (int64_t)rr * ld + cc);
+      upscale16(v, si, w0[u], w1[u]);
+      m = max(m, max(max(bf16x2_absmax_bits(w0[u].x), bf16x2_absmax_bits(w0[u].y)),
+                     max(bf16x2_absmax_bits(w0[u].z), bf16x2_absmax_bits(w0[u].w))));
+      m = max(m, max(max(bf16x2_absmax_bits(w1[u].x), bf16x2_absmax_bits(w1[u].y)),
+                     max(bf16x2_absmax_bits(w1[u].z), bf16x2_absmax_bits(w1[u].w))));
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const int e = pow2_exponent(m);
+  const float f = pow2_neg(e);
+
+  uint8_t* ob = q_out + b * q_bs;
+#pragma unroll
+  for (int u = 0; u < kWChunks; ++u) {
+    const int k = threadIdx.x + u * kWThreads;
+    const int32_t rr = r0 + (k >> 3), cc = c0 + (k & 7) * 16;
+    if (rr < N && cc < K) {
+      u32x4 o;
+      quant8<kNoClip>(w0[u], f, o.x, o.y);
+      quant8<kNoClip>(w1[u], f, o.z, o.w);
+      store16(ob + (int64_t)rr * ld + cc, o);
+    }
+  }
+  if (threadIdx.x == 0)
+    s_out[b * o_bs + (int64_t)i * o_ld + j] = (uint8_t)(e + 127);
+}
+
+}  // namespace
+
+extern "C" mxq_status upscale_fp8_to_bf16(const void* q_fp8, int64_t ld_q,
+                                          const float* scales,
+                                          int64_t scale_row_stride,
+                                          int64_t scale_col_stride,
+                                          int64_t num_rows, int32_t H,
+                                          int32_t group, void* out_bf16,
+                                          int64_t ld_out, void* stream) {
+  if (group != 32 && group != 128) return MXQ_ERR_UNSUPPORTED;
+  if (num_rows < 0 || num_rows > INT32_MAX || H <= 0 || H % group != 0 ||
+      scale_row_stride < 0 || scale_col_stride < 0)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (num_rows == 0) return MXQ_OK;
+  if (q_fp8 == nullptr || scales == nullptr || out_bf16 == nullptr)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (ld_q < H || ld_out < H || ld_q % 16 != 0 || ld_out % 8 != 0 ||
+      !aligned16(q_fp8) || !aligned16(out_bf16))
+    return MXQ_ERR_INVALID_ARGUMENT;
+  const int threads = row_block_threads(H, 16);
+  hipStream_t s = as_stream(stream);
+  const uint8_t* q = static_cast<const uint8_t*>(q_fp8);
+  uint16_t* o = static_cast<uint16_t*>(out_bf16);
+  if (group == 128)
+    upscale_kernel<128><<<(unsigned)num_rows, threads, 0, s>>>(
+        q, ld_q, scales, scale_row_stride, scale_col_stride, H, o, ld_out);
+  else
+    upscale_kernel<32><<<(unsigned)num_rows, threads, 0, s>>>(
+        q, ld_q, scales, scale_row_stride, scale_col_stride, H, o, ld_out);
+  return launch_status();
+}
+
+extern "C" mxq_status requant_weight_block_ue8m0(
+    const void* q_fp8, int64_t ld, int64_t matrix_stride, const float* s_inv,
+    int64_t s_ld, int64_t s_matrix_stride, int32_t num_matrices, int32_t N,
+    int32_t K, int32_t block_n, int32_t block_k, void* q_out,
+    uint8_t* scales_out, int64_t o_ld, int64_t o_matrix_stride,
+    void* stream) {
+  if (block_n != kWBlock || block_k != kWBlock) return MXQ_ERR_UNSUPPORTED;
+  if (num_matrices < 0 || N < 0 || K < 0) return MXQ_ERR_INVALID_ARGUMENT;
+  if (num_matrices == 0 || N == 0 || K == 0) return MXQ_OK;
+  const int64_t nbn = ceil_div(N, kWBlock), nbk = ceil_div(K, kWBlock);
+  if (q_fp8 == nullptr || s_inv == nullptr || q_out == nullptr ||
+      scales_out == nullptr)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (K % 16 != 0 || ld < K || ld % 16 != 0 || !aligned16(q_fp8) ||
+      !aligned16(q_out))
+    return MXQ_ERR_INVALID_ARGUMENT;
+  const int64_t span = (int64_t)(N - 1) * ld + K;  // bytes of one matrix
+  if (num_matrices > 1 && (matrix_stride < span || matrix_stride % 16 != 0))
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (s_ld < nbk || (num_matrices > 1 &&
+                     s_matrix_stride < (nbn - 1) * s_ld + nbk))
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (o_ld < nbk || (num_matrices > 1 &&
+                     o_matrix_stride < (nbn - 1) * o_ld + nbk))
+    return MXQ_ERR_INVALID_ARGUMENT;
+  const int64_t blocks = (int64_t)num_matrices * nbn * nbk;
+  if (blocks > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
+  weight_requant_kernel<<<(unsigned)blocks, kWThreads, 0, as_stream(stream)>>>(
+      static_cast<const uint8_t*>(q_fp8), ld, matrix_stride, s_inv, s_ld,
+      s_matrix_stride, N, K, (int32_t)nbn, (int32_t)nbk,
+      static_cast<uint8_t*>(q_out), scales_out, o_ld, o_matrix_stride);
+  return launch_status();
+}

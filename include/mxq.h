@@ -311,6 +311,56 @@ mxq_status moe_masked_slab_to_expand(
     const float* weights, void* out_bf16, int64_t ld_out, int64_t out_rows,
     void* stream);
 
+/* ------------------------------------------- receive-side upscale (fp8) */
+
+/* fp8 payload with fp32 group scales -> bf16, over the first num_rows rows
+ * [P4 impl. item 3 and the aiter.py snippet: an fp8 dispatch carries
+ * group-128 fp32 scales and is turned back into bf16 for the live rows
+ * (num_local_tokens) before a kernel that consumes bf16].
+ *
+ *   q_fp8    e4m3 [num_rows, ld_q] bytes, ld_q % 16 == 0, 16-byte aligned.
+ *   scales   fp32; scale of (row r, channel c) at
+ *            scales[r*scale_row_stride + (c/group)*scale_col_stride]
+ *            (row-major [rows, H/group]: strides (H/group, 1); MN-major
+ *            [H/group, rows]: strides (1, rows)).
+ *   out      bf16 [num_rows, ld_out], ld_out % 8 == 0, 16-byte aligned:
+ *            out = bf16(dec(q) * s), the exact product rounded once to
+ *            nearest-even (overflow to inf); a NaN result is 0x7FC0.
+ *   group    32 or 128 (others: MXQ_ERR_UNSUPPORTED); H % group == 0.
+ * Rows at or past num_rows are not touched. */
+mxq_status upscale_fp8_to_bf16(const void* q_fp8, int64_t ld_q,
+                               const float* scales, int64_t scale_row_stride,
+                               int64_t scale_col_stride, int64_t num_rows,
+                               int32_t H, int32_t group, void* out_bf16,
+                               int64_t ld_out, void* stream);
+
+/* ------------------------------------------ weight-side UE8M0 requant */
+
+/* Block-scaled fp8 weights -> fp8 with one UE8M0 (power-of-two) scale per
+ * 128 x 128 block [P1 impl. item 1 and the fp8.py snippet: the gate/up and
+ * down expert weights of a standard MoE layer are requantized to UE8M0
+ * block scales at load time, with bf16 as the dequantized type].
+ *
+ *   q_fp8      num_matrices matrices of e4m3 [N, K]: element (m, n, k) at
+ *              m*matrix_stride + n*ld + k bytes; K % 16 == 0, ld % 16 == 0,
+ *              16-byte aligned.
+ *   s_inv      fp32 inverse scales [m][ceil(N/128)][ceil(K/128)] at
+ *              m*s_matrix_stride + i*s_ld + j: weight = dec(q) * s_inv.
+ *   q_out      same geometry as q_fp8; may be q_fp8 itself (in place), must
+ *              not overlap it otherwise.
+ *   scales_out one byte per block at m*o_matrix_stride + i*o_ld + j:
+ *              e + 127, where w = bf16(dec(q) * s_inv) (exact product, one
+ *              rounding), e is the smallest integer with max|w| over the
+ *              block <= 448 * 2^e (clamped to [-127, 127]), and
+ *              q_out = e4m3(w * 2^-e) (nearest-even).
+ *   block_n, block_k must be 128 (others: MXQ_ERR_UNSUPPORTED).
+ * Inputs must be finite (no NaN bytes, finite products). */
+mxq_status requant_weight_block_ue8m0(
+    const void* q_fp8, int64_t ld, int64_t matrix_stride, const float* s_inv,
+    int64_t s_ld, int64_t s_matrix_stride, int32_t num_matrices, int32_t N,
+    int32_t K, int32_t block_n, int32_t block_k, void* q_out,
+    uint8_t* scales_out, int64_t o_ld, int64_t o_matrix_stride, void* stream);
+
 /* ---------------------------------------------------------- diagnostics */
 
 /* The fp32 -> e4m3fn conversion every kernel above uses, exposed so it can

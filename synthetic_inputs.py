@@ -19,6 +19,12 @@ Workloads (shapes follow the pages' DeepSeek-class models: hidden 7168, a
                   [14]*8, group 32 (e8m0)                           seed 404
   requant_combine T=16384, H=4096: fp8 rows with per-token scales 2^U,
                   U ~ U[-8, 4]; 128 experts top-8 uniform, block 128  seed 505
+  fp8_dispatch    24576 x 7168 e4m3 rows (3072 x 8 padded receive buffer)
+                  with group-128 fp32 scales, upscaled over the first
+                  num_local_tokens rows                             seed 606
+  block_weights   e4m3 expert weights [32, 4096, 7168] (gate/up) and
+                  [32, 7168, 2048] (down), one fp32 inverse scale per
+                  128 x 128 block                                   seed 707
 """
 from __future__ import annotations
 
@@ -28,6 +34,8 @@ import numpy as np
 import torch
 
 SEEDS = {
+    "fp8_dispatch": 606,
+    "block_weights": 707,
     "tiny": 101,
     "decode_masked": 202,
     "prefill_compact": 303,
@@ -238,3 +246,60 @@ def poison_padding_rows(y_bits: np.ndarray, m_indices: np.ndarray):
     """Set every padding row (m_indices == -1) to NaN (bf16 0x7FC0)."""
     y_bits[np.asarray(m_indices) < 0] = np.uint16(0x7FC0)
     return y_bits
+
+
+def random_e4m3_bytes(rng: np.random.Generator, shape,
+                      exp_mean: float = 11.0, exp_sd: float = 2.0):
+    """Finite e4m3fn bytes drawn field by field: random sign, exponent field
+    ~ round(N(exp_mean, exp_sd)) clipped to [0, 15], uniform mantissa; the
+    NaN pattern (exponent 15, mantissa 7) is redrawn as mantissa 6.  A
+    block of a few thousand bytes almost surely holds exponent 15 (values
+    256..448), like a block quantized to the full e4m3 range."""
+    ef = np.clip(np.rint(rng.normal(exp_mean, exp_sd, shape)), 0, 15).astype(
+        np.uint8)
+    m = rng.integers(0, 8, shape, dtype=np.uint8)
+    m = np.where((ef == 15) & (m == 7), np.uint8(6), m)
+    sign = (rng.random(shape) < 0.5).astype(np.uint8) << 7
+    return (sign | (ef << 3) | m).astype(np.uint8)
+
+
+def random_e4m3_bytes_device(seed: int, shape, device) -> torch.Tensor:
+    """Finite e4m3fn bytes drawn uniformly on a device (torch generator):
+    0..253 with 0x7F..0xFD moved up by one, so 0x7F and 0xFF never occur."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    v = torch.randint(0, 254, shape, dtype=torch.int16, device=device,
+                      generator=g)
+    return (v + (v >= 0x7F).to(torch.int16)).to(torch.uint8)
+
+
+def group_scales_f32(rng: np.random.Generator, shape, lo: float = 2.0 ** -14,
+                     hi: float = 2.0 ** -6) -> np.ndarray:
+    """Positive fp32 scales, log-uniform in [lo, hi) (an amax / 448 range
+    for bf16 activations or weights)."""
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), shape)).astype(
+        np.float32)
+
+
+@dataclass
+class Fp8Dispatch:
+    q: np.ndarray          # uint8 [rows, H]
+    scales: np.ndarray     # float32 [rows, H / 128]
+    num_local_tokens: int
+
+
+def fp8_dispatch(seed: int = SEEDS["fp8_dispatch"], rows: int = 24576,
+                 H: int = 7168, num_local_tokens: int = 8192) -> Fp8Dispatch:
+    rng = np.random.default_rng(seed)
+    return Fp8Dispatch(random_e4m3_bytes(rng, (rows, H)),
+                       group_scales_f32(rng, (rows, H // 128)),
+                       num_local_tokens)
+
+
+def block_weights(seed: int, B: int, N: int, K: int, block: int = 128):
+    """(q bytes [B, N, K], s_inv fp32 [B, ceil(N/128), ceil(K/128)])."""
+    rng = np.random.default_rng(seed)
+    q = random_e4m3_bytes(rng, (B, N, K))
+    s = group_scales_f32(rng, (B, -(-N // block), -(-K // block)),
+                         2.0 ** -16, 2.0 ** -8)
+    return q, s

@@ -139,6 +139,47 @@ def test_scatter_quant_ex_validation(mxq):
     assert call(rows=0, q=None, s=None, rs=4, c4=0) == 0
 
 
+def test_upscale_and_weight_requant_validation(mxq):
+    L = mxq.lib()
+
+    def up(q=FAKE, ld_q=256, s=FAKE, rs=2, cs=1, rows=4, H=256, G=128,
+           o=FAKE, ld_o=256):
+        return L.upscale_fp8_to_bf16(q, ld_q, s, rs, cs, rows, H, G, o, ld_o,
+                                     None)
+
+    assert up(G=64) == UNSUPPORTED
+    assert up(H=200) == INVALID                # not a multiple of 128
+    assert up(rows=-1) == INVALID
+    assert up(ld_q=264 - 16 - 8) == INVALID    # ld_q < H
+    assert up(ld_q=264) == INVALID             # not 16-byte rows
+    assert up(ld_o=260) == INVALID             # bf16 rows not 16-byte
+    assert up(o=FAKE + 2) == INVALID
+    assert up(s=None) == INVALID
+    assert up(rs=-1) == INVALID
+    assert up(rows=0, q=None, s=None, o=None) == 0
+    assert up(G=32, H=96, ld_q=96, ld_o=96, rows=0) == 0
+
+    def wr(q=FAKE, ld=256, qbs=256 * 256, s=FAKE, sld=2, sbs=4, B=2, N=256,
+           K=256, bn=128, bk=128, qo=FAKE, so=FAKE, old=2, obs=4):
+        return L.requant_weight_block_ue8m0(q, ld, qbs, s, sld, sbs, B, N, K,
+                                            bn, bk, qo, so, old, obs, None)
+
+    assert wr(bn=64) == UNSUPPORTED
+    assert wr(bk=256) == UNSUPPORTED
+    assert wr(K=200, ld=208) == INVALID        # K % 16
+    assert wr(ld=250) == INVALID               # ld < K
+    assert wr(qbs=256 * 255) == INVALID        # matrices overlap
+    assert wr(sld=1) == INVALID
+    assert wr(sbs=3) == INVALID
+    assert wr(old=1) == INVALID
+    assert wr(obs=3) == INVALID
+    assert wr(qo=FAKE + 4) == INVALID
+    assert wr(so=None) == INVALID
+    assert wr(B=-1) == INVALID
+    assert wr(N=0) == 0
+    assert wr(B=0, q=None, s=None, qo=None, so=None) == 0
+
+
 def test_layout_validation(mxq):
     L = mxq.lib()
 
