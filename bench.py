@@ -74,25 +74,6 @@ def bytes_combine(T, K, H, assignments, out_bytes=2):
 
 # ---------------------------------------------------------------- helpers
 
-class EventTimer:
-    """HIP events recorded on the current stream (the one the library's
-    kernels are launched on)."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.marks = []
-
-    def mark(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record(self.torch.cuda.current_stream())
-        self.marks.append(e)
-        return e
-
-    @staticmethod
-    def ms(a, b):
-        return a.elapsed_time(b)
-
-
 def time_calls(torch, fn, reps=20, warmup=3):
     for _ in range(warmup):
         fn()
@@ -200,44 +181,68 @@ def main():
     copy_gbs = 2 * cbuf_a.numel() / (copy_us * 1e-6) / 1e9
     del cbuf_a, cbuf_b
 
-    timer = EventTimer(torch)
-
-    def step(record):
-        if record:
-            timer.mark()
+    def step():
         lay = mxq.moe_layout(ids, 0, E, "compact", num_rows=R, out=lay_out,
                              workspace=ws)
-        if record:
-            timer.mark()
         mxq.moe_scatter_quant(x, lay["src2dst"], R, "ue8m0_g128", q=q,
                               scales=s)
-        if record:
-            timer.mark()
         mxq.moe_combine(y, lay["src2dst"], w, out=out)
-        if record:
-            timer.mark()
+
+    # The timed loop calls the C entry points directly with arguments
+    # prepared once (the same calls the wrappers above make), and its events
+    # are created beforehand, so the host issues a step in a few
+    # microseconds and stays ahead of the GPU.
+    L = mxq.lib()
+    hs = torch.cuda.current_stream().cuda_stream
+    p = {k: t.data_ptr() for k, t in lay_out.items()}
+    lay_args = (ids.data_ptr(), T, K, 0, E, mxq.LAYOUT_KINDS["compact"],
+                b.block_e, 0, R, p["counts"], p["expert_offsets"],
+                p["m_indices"], p["masked_m"], p["src2dst"],
+                p["overflow_flag"], ws.data_ptr(), ws.numel(), hs)
+    sq_args = (x.data_ptr(), H, T, H, p["src2dst"], K,
+               mxq.SCALE_FORMATS["ue8m0_g128"][0], q.data_ptr(), H,
+               s.data_ptr(), H // G, R, hs)
+    cb_args = (y.data_ptr(), H, R, p["src2dst"], w.data_ptr(), T, K, H,
+               out.data_ptr(), H, mxq.OUT_DTYPES[torch.bfloat16], hs)
+    ev = [torch.cuda.Event(enable_timing=True)
+          for _ in range(4 * args.steps)]
+    cur = torch.cuda.current_stream()
+
+    def step_fast(i):
+        ev[4 * i].record(cur)
+        st = L.moe_layout(*lay_args)
+        ev[4 * i + 1].record(cur)
+        st |= L.moe_scatter_quant(*sq_args)
+        ev[4 * i + 2].record(cur)
+        st |= L.moe_combine(*cb_args)
+        ev[4 * i + 3].record(cur)
+        return st
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
+    status = 0
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
+    for i in range(args.steps):
+        status |= step_fast(i)
+    t_issue = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t0
-    m = timer.marks
-    lay_ms = [m[4 * i].elapsed_time(m[4 * i + 1]) for i in range(args.steps)]
-    sq_ms = [m[4 * i + 1].elapsed_time(m[4 * i + 2])
+    if status != 0:
+        raise RuntimeError("a library call in the timed loop failed "
+                           "(status bits %d)" % status)
+    lay_ms = [ev[4 * i].elapsed_time(ev[4 * i + 1])
+              for i in range(args.steps)]
+    sq_ms = [ev[4 * i + 1].elapsed_time(ev[4 * i + 2])
              for i in range(args.steps)]
-    cb_ms = [m[4 * i + 2].elapsed_time(m[4 * i + 3])
+    cb_ms = [ev[4 * i + 2].elapsed_time(ev[4 * i + 3])
              for i in range(args.steps)]
     step_ms = wall_s * 1e3 / args.steps
     ev_step_ms = float(np.mean(lay_ms) + np.mean(sq_ms) + np.mean(cb_ms))
 
     # the same step captured once in a hipGraph and replayed (no per-kernel
     # host launch cost); reported beside the eager timed region
-    graph_ms = graph_step_ms(torch, lambda: step(False), args.warmup,
-                             args.steps)
+    graph_ms = graph_step_ms(torch, step, args.warmup, args.steps)
 
     value = B_step / (step_ms * 1e-3) / 1e9
     cb_gbs = B_cb / (np.mean(cb_ms) * 1e-3) / 1e9
@@ -269,6 +274,7 @@ def main():
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "assignments_per_s": round(A / (step_ms * 1e-3), 1),
+        "host_issue_ms_per_step": round(t_issue * 1e3 / args.steps, 4),
         "graph_replay": {"ms_per_step": round(graph_ms, 4),
                          "gbs": round(B_step / (graph_ms * 1e-3) / 1e9, 2)},
         "scatter_quant_plus_combine": {
@@ -298,10 +304,15 @@ def main():
             "traffic": traffic,
         },
     }
+    variants = None
+    if not args.no_rows:
+        variants = scale_variant_rows(torch, mxq, x, lay_out["src2dst"], R,
+                                      H, q, B_sq, dev)
     del q, s, out
 
     if not args.no_rows:
         result["rows"] = other_rows(torch, mxq, si, dev)
+        result["rows"]["scale_variants"] = variants
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, si, b, y, R, B_step,
@@ -310,6 +321,28 @@ def main():
 
 
 # ------------------------------------------------- separately timed rows
+
+def scale_variant_rows(torch, mxq, x, src2dst, R, H, q, B_sq, dev):
+    """The prefill scatter under each exponent rule and scale placement,
+    timed back to back (the plain entry point beside them, timed the same
+    way)."""
+    out = {"workload": "prefill scatter (8192 x 7168 -> 98048 rows, "
+                       "UE8M0 group-128), back-to-back calls",
+           "algorithmic_bytes": B_sq}
+    s_rows = torch.empty((R, H // 128), dtype=torch.uint8, device=dev)
+    s_mn = mxq.packed_mn_scales(R, H // 128, dev)
+    us = time_calls(torch, lambda: mxq.moe_scatter_quant(
+        x, src2dst, R, "ue8m0_g128", q=q, scales=s_rows))
+    out["moe_scatter_quant_us"] = round(us, 2)
+    for rule in ("no_clip", "ocp_floor"):
+        for layout, sc in (("rows", s_rows), ("packed_mn", s_mn)):
+            us = time_calls(torch, lambda: mxq.moe_scatter_quant_ex(
+                x, src2dst, R, "ue8m0_g128", rule, layout, q=q, scales=sc))
+            out["%s/%s_us" % (rule, layout)] = round(us, 2)
+            out["%s/%s_gbs" % (rule, layout)] = round(
+                B_sq / (us * 1e-6) / 1e9, 2)
+    return out
+
 
 def other_rows(torch, mxq, si, dev):
     rows = {}
@@ -416,6 +449,49 @@ def other_rows(torch, mxq, si, dev):
         "masked_slab_to_expand_us": round(us_b, 2),
         "slab_to_expand_bytes": real * (2 * 7168 * 2 + 4),
         "m_indices_from_psum_us": round(us_m, 2)}
+
+    # receive-side upscale: fp8 + group-128 fp32 scales -> bf16 over the
+    # live rows of the 3072 x 8 padded receive buffer
+    rows_u, H_u, n_u = 24576, 7168, 8192
+    qu = si.random_e4m3_bytes_device(si.SEEDS["fp8_dispatch"], (rows_u, H_u),
+                                     dev)
+    su = torch.from_numpy(si.group_scales_f32(
+        np.random.default_rng(si.SEEDS["fp8_dispatch"]),
+        (rows_u, H_u // 128))).to(dev)
+    ou = torch.empty((rows_u, H_u), dtype=torch.bfloat16, device=dev)
+    us = time_calls(torch, lambda: mxq.upscale_fp8_to_bf16(qu, su, n_u,
+                                                          out=ou))
+    byts = n_u * (H_u + 4 * (H_u // 128) + 2 * H_u)
+    rows["upscale"] = {
+        "workload": "24576 x 7168 fp8 receive buffer, group-128 fp32 scales, "
+                    "first 8192 rows upscaled to bf16",
+        "us": round(us, 2), "algorithmic_bytes": byts,
+        "gbs": round(byts / (us * 1e-6) / 1e9, 2)}
+    del qu, su, ou
+
+    # weight-side UE8M0 block requant of 32 local experts' gate/up and down
+    # weights (load time)
+    wr = {"workload": "32 experts: gate/up [32, 4096, 7168] and down "
+                      "[32, 7168, 2048] e4m3 with 128 x 128 fp32 block "
+                      "scales -> UE8M0 block scales"}
+    for name, shape in (("gate_up", (32, 4096, 7168)),
+                        ("down", (32, 7168, 2048))):
+        qw = si.random_e4m3_bytes_device(si.SEEDS["block_weights"], shape,
+                                         dev)
+        B_, N_, K_ = shape
+        sw = torch.from_numpy(si.group_scales_f32(
+            np.random.default_rng(si.SEEDS["block_weights"]),
+            (B_, N_ // 128, K_ // 128), 2.0 ** -16, 2.0 ** -8)).to(dev)
+        qo = torch.empty_like(qw)
+        so = torch.empty(sw.shape, dtype=torch.uint8, device=dev)
+        us = time_calls(torch, lambda: mxq.requant_weight_block_ue8m0(
+            qw, sw, q_out=qo, scales_out=so), reps=10)
+        nblk = B_ * (N_ // 128) * (K_ // 128)
+        byts = 2 * qw.numel() + 5 * nblk
+        wr[name] = {"us": round(us, 2), "algorithmic_bytes": byts,
+                    "gbs": round(byts / (us * 1e-6) / 1e9, 2)}
+        del qw, sw, qo, so
+    rows["weight_requant"] = wr
 
     # large combine: 16384 tokens x 4096 from 147328 rows, top-8 of 128
     cids, cw = si.large_combine_routing()
