@@ -53,6 +53,9 @@ def parse_args():
     p.add_argument("--no-rows", action="store_true",
                    help="skip the separately timed rows")
     p.add_argument("--cpu-repeats", type=int, default=3)
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the step, time masked against compact "
+                        "layouts over a range of token counts")
     return p.parse_args()
 
 
@@ -74,18 +77,30 @@ def bytes_combine(T, K, H, assignments, out_bytes=2):
 
 # ---------------------------------------------------------------- helpers
 
-def time_calls(torch, fn, reps=20, warmup=3):
+def time_calls(torch, fn, reps=20, warmup=3, replays=5):
+    """GPU time per call of fn, in microseconds: reps calls captured in one
+    hipGraph, timed with events around each replay (median of replays), so
+    host launch cost between calls is not counted."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    ev[0].record()
-    for i in range(reps):
-        fn()
-        ev[i + 1].record()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
     torch.cuda.synchronize()
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
-    return float(np.median(per)) * 1e3  # microseconds
+    per = []
+    for _ in range(replays):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / reps)
+    del g
+    return float(np.median(per)) * 1e3
 
 
 def graph_step_ms(torch, fn, warmup, steps):
@@ -147,6 +162,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.sweep:
+        print(json.dumps(layout_sweep(torch, mxq, si, dev)), flush=True)
+        return
 
     # ---------------------------------------------------------- inputs
     b = si.prefill_compact()
@@ -318,6 +337,69 @@ def main():
         result["cpu_baseline"] = cpu_baseline(torch, si, b, y, R, B_step,
                                               args.cpu_repeats)
     print(json.dumps(result), flush=True)
+
+
+# ------------------------------------------- masked vs compact sweep
+
+SWEEP_T = (256, 1024, 4096, 8192, 16384)
+SWEEP_CASES = ((128, 128, "128 local experts, no expert parallelism"),
+               (48, 384, "48 local experts of 384 (one GPU of eight)"))
+
+
+def layout_sweep(torch, mxq, si, dev, H=7168, K=8):
+    """Layout + scatter-quant + combine time per step under the masked and
+    the compact layout, for each token count: the masked slab holds
+    capacity T rows per local expert (the largest possible count, so any
+    routing fits a static buffer); the compact buffer holds the static
+    bound of the compact layout."""
+    out = {"metric": "masked vs compact dispatch preprocessing time",
+           "unit": "us", "hidden": H, "topk": K,
+           "routing": "uniform top-8 over the global experts",
+           "timing": "per call, 20 calls captured in a hipGraph, median "
+                     "of 5 replays",
+           "cases": []}
+    for e_loc, e_glob, label in SWEEP_CASES:
+        case = {"local_experts": e_loc, "global_experts": e_glob,
+                "label": label, "points": []}
+        for T in SWEEP_T:
+            rng = np.random.default_rng(1000 * e_loc + T)
+            ids_h = si.uniform_topk(rng, T, e_glob, K)
+            ids = torch.from_numpy(ids_h).to(dev)
+            w = torch.from_numpy(si.softmax_weights(rng, T, K)).to(dev)
+            x = si.gaussian_bf16_device(T, (T, H), dev)
+            local = int(((ids_h >= 0) & (ids_h < e_loc)).sum())
+            pt = {"T": T, "local_assignments": local}
+            for kind, cap in (("compact", 0), ("masked", T)):
+                rows = (mxq.moe_compact_row_bound(T * K, e_loc, 128)
+                        if kind == "compact" else e_loc * cap)
+                lay = mxq.moe_layout(ids, 0, e_loc, kind, capacity=cap,
+                                     num_rows=rows)
+                q = torch.empty((rows, H), dtype=torch.uint8, device=dev)
+                sc = torch.empty((rows, H // 128), dtype=torch.uint8,
+                                 device=dev)
+                y = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+                y.view(torch.int16).fill_(0x3F80)
+                o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+                t_l = time_calls(torch, lambda: mxq.moe_layout(
+                    ids, 0, e_loc, kind, capacity=cap, num_rows=rows,
+                    out=lay))
+                t_s = time_calls(torch, lambda: mxq.moe_scatter_quant(
+                    x, lay["src2dst"], rows, q=q, scales=sc))
+                t_c = time_calls(torch, lambda: mxq.moe_combine(
+                    y, lay["src2dst"], w, out=o))
+                pt[kind] = {"rows": rows,
+                            "buffer_gib": round(rows * H * 3 / 2 ** 30, 2),
+                            "layout_us": round(t_l, 2),
+                            "scatter_quant_us": round(t_s, 2),
+                            "combine_us": round(t_c, 2),
+                            "total_us": round(t_l + t_s + t_c, 2)}
+                del lay, q, sc, y, o
+            pt["compact_over_masked"] = round(
+                pt["compact"]["total_us"] / pt["masked"]["total_us"], 4)
+            case["points"].append(pt)
+            del ids, w, x
+        out["cases"].append(case)
+    return out
 
 
 # ------------------------------------------------- separately timed rows
