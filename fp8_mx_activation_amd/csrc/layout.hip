@@ -7,7 +7,8 @@
 // slots with masked_m, overflow fails fast).  Slots inside an expert follow
 // ascending flat assignment index t*K + j.
 //
-// Two launches whose grids depend only on T*K, E and num_rows:
+// Two launches whose grids depend only on T*K, E and num_rows (one launch,
+// the assign kernel in its SINGLE form, when T*K <= 8192):
 //   layout_hist_kernel    one block per chunk of assignments: LDS histogram
 //                         of the chunk's local experts -> cnt[chunk][E].
 //   layout_assign_kernel  one block of 16 wavefronts per chunk, plus enough
@@ -60,6 +61,49 @@ __global__ __launch_bounds__(256) void layout_hist_kernel(
     cnt[(int64_t)blockIdx.x * E + i] = hist[i];
 }
 
+// B: region starts from each expert's total (thread e < E holds total_e), a
+// block-wide scan of the padded sizes into off[0..E]; block 0 also
+// publishes counts, region starts, masked_m and the overflow flag.
+__device__ __forceinline__ void region_scan(
+    int total, int32_t E, int32_t kind, int32_t block_e, int32_t cap,
+    int32_t* off, int32_t* wsum, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ masked_m,
+    int32_t* __restrict__ overflow) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  int padded = 0;
+  if (tid < E)
+    padded = kind == 0 ? (total + block_e - 1) / block_e * block_e : cap;
+  int incl = padded;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0, grand = 0;
+  const int nwaves = blockDim.x >> 6;
+  for (int w = 0; w < nwaves; ++w) {
+    before += (w < wv) ? wsum[w] : 0;
+    grand += wsum[w];
+  }
+  if (tid < E) off[tid] = before + incl - padded;
+  if (tid == 0) off[E] = grand;
+  if (blockIdx.x == 0) {
+    if (tid < E) {
+      counts[tid] = total;
+      offsets[tid] = before + incl - padded;
+      if (masked_m != nullptr)
+        masked_m[tid] = kind == 1 ? min(total, cap) : total;
+    }
+    if (tid == 0) offsets[E] = grand;
+    const int ovf = (tid < E && kind == 1 && total > cap) ? 1 : 0;
+    const int any = __syncthreads_or(ovf);
+    if (tid == 0) *overflow = any ? 1 : 0;
+  }
+}
+
 // Slots: one block of kAssignWaves wavefronts per chunk.  Each wavefront
 // owns a contiguous run of whole 64-assignment steps; it ranks its lanes
 // within each step (ballot multi-split) and among its own earlier steps, and
@@ -67,6 +111,12 @@ __global__ __launch_bounds__(256) void layout_hist_kernel(
 // prefix-summed over the wavefronts, so a lane's slot is
 // chunk base + count of the same expert in earlier wavefronts + its rank in
 // its wavefront: flat order, no atomics, no serial chain across wavefronts.
+//
+// SINGLE: all assignments form one chunk (T*K <= kChunkMax) and no
+// histogram pass runs.  Every block ranks that chunk (C1), takes the totals
+// from the per-wavefront counts (C2) and then scans the regions (B); block 0
+// alone writes src2dst.
+template <bool SINGLE>
 __global__ __launch_bounds__(1024) void layout_assign_kernel(
     const int32_t* __restrict__ ids, int64_t A, int32_t begin, int32_t E,
     int32_t nbits, int32_t kind, int32_t block_e, int32_t cap,
@@ -90,8 +140,9 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int c = blockIdx.x;
+  const int c = SINGLE ? 0 : (int)blockIdx.x;
   const bool has_chunk = c < nc;
+  const bool writer = SINGLE ? blockIdx.x == 0 : has_chunk;
   const int64_t c_begin = (int64_t)c * chunk;
   const int64_t c_end = has_chunk ? min(c_begin + (int64_t)chunk, A) : c_begin;
   const int64_t w_begin = c_begin + (int64_t)wv * steps_per_wave * 64;
@@ -108,7 +159,7 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
   // A: totals and this chunk's first slots from the chunk counts.  Up to
   // four groups of threads per expert split the chunks; each issues its
   // loads a batch at a time.
-  {
+  if constexpr (!SINGLE) {
     const int er = (E + 63) / 64 * 64;
     const int nparts = max(1, (int)blockDim.x / er);
     const int part = tid / er;
@@ -145,37 +196,8 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
       tot[tid] = total;
       cbase[tid] = first;
     }
-    // B: region starts, a block-wide scan of the padded sizes
-    int padded = 0;
-    if (tid < E)
-      padded = kind == 0 ? (total + block_e - 1) / block_e * block_e : cap;
-    int incl = padded;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
-    int before = 0, grand = 0;
-    const int nwaves = blockDim.x >> 6;
-    for (int w = 0; w < nwaves; ++w) {
-      before += (w < wv) ? wsum[w] : 0;
-      grand += wsum[w];
-    }
-    if (tid < E) off[tid] = before + incl - padded;
-    if (tid == 0) off[E] = grand;
-    if (blockIdx.x == 0) {
-      if (tid < E) {
-        counts[tid] = total;
-        offsets[tid] = before + incl - padded;
-        if (masked_m != nullptr)
-          masked_m[tid] = kind == 1 ? min(total, cap) : total;
-      }
-      if (tid == 0) offsets[E] = grand;
-      const int ovf = (tid < E && kind == 1 && total > cap) ? 1 : 0;
-      const int any = __syncthreads_or(ovf);
-      if (tid == 0) *overflow = any ? 1 : 0;
-    }
+    region_scan(total, E, kind, block_e, cap, off, wsum, counts, offsets,
+                masked_m, overflow);
   }
   __syncthreads();
   for (int i = tid; i < kAssignWaves * E; i += blockDim.x) cnt[i] = 0;
@@ -222,11 +244,25 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
         cnt[w * E + e] = (uint16_t)run;
         run += v;
       }
+      if (SINGLE) {
+        tot[e] = run;
+        cbase[e] = 0;
+      }
     }
+  } else if (SINGLE) {
+    for (int e = tid; e < E; e += blockDim.x) {
+      tot[e] = 0;
+      cbase[e] = 0;
+    }
+  }
+  if constexpr (SINGLE) {
+    __syncthreads();
+    region_scan(tid < E ? tot[tid] : 0, E, kind, block_e, cap, off, wsum,
+                counts, offsets, masked_m, overflow);
   }
   __syncthreads();
   // C3: destinations
-  if (has_chunk) {
+  if (has_chunk && writer) {
 #pragma unroll
     for (int st = 0; st < kMaxStepsPerWave; ++st) {
       if (st >= steps_per_wave) break;
@@ -333,17 +369,23 @@ extern "C" mxq_status moe_layout(
   hipStream_t s = as_stream(stream);
   int32_t* chunk_cnt = static_cast<int32_t*>(workspace);
   const int32_t cap = kind == MXQ_LAYOUT_MASKED ? capacity : 0;
-  if (g.nc > 0) {
+  const bool single = A <= kChunkMax;
+  if (g.nc > 0 && !single) {
     layout_hist_kernel<<<g.nc, 256, (size_t)E * sizeof(int32_t), s>>>(
         topk_ids, A, expert_begin, E, g.chunk, chunk_cnt);
     if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;
   }
+  // a single chunk holds every assignment (whole 1024-assignment groups)
+  const int32_t chunk = single ? (int32_t)(ceil_div(A > 0 ? A : 1, kChunkMin) *
+                                           kChunkMin)
+                               : g.chunk;
+  const int32_t nc = single ? (A > 0 ? 1 : 0) : g.nc;
   // One block per chunk (at least one: block 0 publishes the per-expert
   // outputs); more blocks (up to 64) if the m_indices fill needs them.
   // Each of the 16 wavefronts of a block takes steps_per_wave steps.
   const int32_t steps_per_wave =
-      (int32_t)ceil_div(ceil_div(g.chunk, 64), kAssignWaves);
-  int64_t blocks = g.nc > 0 ? g.nc : 1;
+      (int32_t)ceil_div(ceil_div(chunk, 64), kAssignWaves);
+  int64_t blocks = nc > 0 ? nc : 1;
   if (m_indices != nullptr) {
     int64_t fill_blocks = ceil_div(num_rows, 4096);
     if (fill_blocks > 64) fill_blocks = 64;
@@ -352,9 +394,15 @@ extern "C" mxq_status moe_layout(
   const size_t fixed = (size_t)(3 * E + 1) * sizeof(int32_t) +
                        (size_t)kAssignWaves * E * sizeof(uint16_t);
   const int32_t tbl_cap = (int32_t)((kAssignLds - fixed) / sizeof(int32_t));
-  layout_assign_kernel<<<(unsigned)blocks, 1024, kAssignLds, s>>>(
-      topk_ids, A, expert_begin, E, nbits, (int32_t)kind, block_e, cap,
-      num_rows, g.chunk, g.nc, steps_per_wave, tbl_cap, chunk_cnt, counts,
-      expert_offsets, masked_m, overflow_flag, m_indices, src2dst);
+  if (single)
+    layout_assign_kernel<true><<<(unsigned)blocks, 1024, kAssignLds, s>>>(
+        topk_ids, A, expert_begin, E, nbits, (int32_t)kind, block_e, cap,
+        num_rows, chunk, nc, steps_per_wave, tbl_cap, nullptr, counts,
+        expert_offsets, masked_m, overflow_flag, m_indices, src2dst);
+  else
+    layout_assign_kernel<false><<<(unsigned)blocks, 1024, kAssignLds, s>>>(
+        topk_ids, A, expert_begin, E, nbits, (int32_t)kind, block_e, cap,
+        num_rows, chunk, nc, steps_per_wave, tbl_cap, chunk_cnt, counts,
+        expert_offsets, masked_m, overflow_flag, m_indices, src2dst);
   return launch_status();
 }

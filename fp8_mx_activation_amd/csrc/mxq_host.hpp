@@ -69,8 +69,10 @@ inline LayoutGeom layout_geom(int64_t A) {
   return g;
 }
 
-// Workspace: per-chunk expert counts [nc][E] (none without assignments).
+// Workspace: per-chunk expert counts [nc][E]; none when every assignment
+// fits one chunk (A <= kChunkMax), which the layout handles in one launch.
 inline size_t layout_workspace_bytes(int64_t A, int32_t E) {
+  if (A <= kChunkMax) return 0;
   LayoutGeom g = layout_geom(A);
   return (size_t)g.nc * (size_t)(E > 0 ? E : 0) * sizeof(int32_t);
 }

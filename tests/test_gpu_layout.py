@@ -111,8 +111,24 @@ def test_empty_batch(ora):
     assert (host(got["m_indices"]) == -1).all()
 
 
+@pytest.mark.parametrize("T,K,E", [(1024, 8, 1024), (1025, 8, 1024),
+                                   (683, 12, 300), (129, 8, 256),
+                                   (8192, 1, 7), (128, 8, 32)])
+def test_single_chunk_boundary(ora, T, K, E):
+    """Around T*K = 8192, where one launch (every block ranking the single
+    chunk) gives way to the histogram + slots pair: 8192 and 1032 take the
+    single path, 8200 and 8196 the two-launch path; masked capacity small
+    enough to overflow."""
+    rng = np.random.default_rng(T * K + E)
+    ids = si.zipf_topk(rng, T, E, K) if E >= 2 * K else si.uniform_topk(
+        rng, T, E, K)
+    run_both(ora, ids, 0, E, "compact")
+    run_both(ora, ids, 0, E, "compact", block_e=1)
+    got, ref = run_both(ora, ids, 0, E, "masked", cap=max(1, T * K // E // 2))
+
+
 def test_many_assignments(ora):
-    """Two million assignments: 64 chunks of 32768, long in-chunk walks."""
+    """Two million assignments: 256 chunks of 8192."""
     rng = np.random.default_rng(9)
     ids = si.zipf_topk(rng, 262144, 256, 8)
     run_both(ora, ids, 0, 256, "compact")
