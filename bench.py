@@ -103,6 +103,27 @@ def time_calls(torch, fn, reps=20, warmup=3, replays=5):
     return float(np.median(per)) * 1e3
 
 
+def time_calls_cold(torch, fn, flush, reps=10, warmup=2):
+    """GPU time per call of fn with the 256 MB last-level cache (MALL) and
+    the L2s flushed before each call by reading `flush` (512 MB, written
+    once beforehand, so the evicting lines are clean and nothing is written
+    back during the call): events bracket the call alone; median over
+    reps."""
+    for _ in range(warmup):
+        fn()
+    flush_f = flush.view(torch.float32)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        flush_f.sum()
+        ev[i][0].record()
+        fn()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+
 def graph_step_ms(torch, fn, warmup, steps):
     """Capture fn once in a hipGraph; time `steps` replays."""
     side = torch.cuda.Stream()
@@ -428,6 +449,8 @@ def scale_variant_rows(torch, mxq, x, src2dst, R, H, q, B_sq, dev):
 
 def other_rows(torch, mxq, si, dev):
     rows = {}
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
     # masked decode slab: one GPU's 32 of 256 experts, T=128
     d = si.decode_masked()
     ids = torch.from_numpy(d.topk_ids).to(dev)
@@ -467,6 +490,13 @@ def other_rows(torch, mxq, si, dev):
                      "rows_per_s": round(n / (us * 1e-6), 1),
                      "algorithmic_bytes": byts}
     res["padded_grid_equivalent_bytes"] = 24576 * (7168 * 2 + 7168 + 224)
+    # the same quant over every row of the padded buffer (what a receiver
+    # that sizes its grid by the buffer pays)
+    lc = torch.full((8,), 3072, dtype=torch.int32, device=dev)
+    us_pad = time_calls(torch, lambda: mxq.mx_quant_live_rows(
+        xs, 8, lc, q=qs, scales=ss), reps=5)
+    res["padded_grid_us"] = round(us_pad, 2)
+    res["padded_over_live_14x8"] = round(us_pad / res["14x8"]["us"], 1)
     res["workload"] = ("24576 x 7168 bf16 padded buffer = 8 segments of "
                        "3072 rows, e8m0 group-32 (224 scales/row)")
     rows["live_rows_mx"] = res
@@ -483,12 +513,18 @@ def other_rows(torch, mxq, si, dev):
     us = time_calls(torch, lambda: mxq.requant_per_token_to_per_tensor(
         qi, sc, q_out=qo, tensor_scale=Sd, workspace=rws))
     byts = 2 * qi.numel() + qi.shape[0] * 4 + 4
+    us_cold = time_calls_cold(torch, lambda: mxq.requant_per_token_to_per_tensor(
+        qi, sc, q_out=qo, tensor_scale=Sd, workspace=rws), flush)
     rows["requant"] = {"workload": "16384 x 4096 fp8, per-token scales "
                                    "2^U, U~U[-8,4]",
                        "us": round(us, 2), "algorithmic_bytes": byts,
                        "gbs": round(byts / (us * 1e-6) / 1e9, 2),
-                       "note": "input (64 MiB) stays in the 256 MB MALL "
-                               "across the two passes and back-to-back calls"}
+                       "cold_us": round(us_cold, 2),
+                       "cold_gbs": round(byts / (us_cold * 1e-6) / 1e9, 2),
+                       "note": "warm: the 64 MiB input stays in the 256 MB "
+                               "MALL across the two passes and back-to-back "
+                               "calls; cold: MALL flushed by reading 512 MB "
+                               "before each call"}
     del qi, qo
 
     # psum (expanded) layout repack at the decode shape: the dispatcher's
@@ -584,11 +620,17 @@ def other_rows(torch, mxq, si, dev):
     ol = torch.empty((16384, 4096), dtype=torch.bfloat16, device=dev)
     us = time_calls(torch, lambda: mxq.moe_combine(yl, lay["src2dst"], wd,
                                                    out=ol))
+    us_cold = time_calls_cold(torch, lambda: mxq.moe_combine(
+        yl, lay["src2dst"], wd, out=ol), flush)
     byts = bytes_combine(16384, 8, 4096, 16384 * 8)
     rows["large_combine"] = {"workload": "T=16384, hidden 4096, 128 experts "
                                          "top-8, 147328-row layout",
                              "us": round(us, 2), "algorithmic_bytes": byts,
-                             "gbs": round(byts / (us * 1e-6) / 1e9, 2)}
+                             "gbs": round(byts / (us * 1e-6) / 1e9, 2),
+                             "cold_us": round(us_cold, 2),
+                             "cold_gbs": round(byts / (us_cold * 1e-6) / 1e9,
+                                               2)}
+    del flush
     return rows
 
 
@@ -608,6 +650,14 @@ def cpu_baseline(torch, si, b, y_dev, R, B_step, repeats):
         oracle.combine(y_host, lay["src2dst"], b.topk_weights)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
+    # the same work on one thread, once
+    oracle.set_threads(1)
+    t0 = time.perf_counter()
+    lay = oracle.moe_layout(b.topk_ids, 0, b.n_local, "compact")
+    oracle.scatter_quant(b.x, lay["src2dst"], b.group, R)
+    oracle.combine(y_host, lay["src2dst"], b.topk_weights)
+    t1 = time.perf_counter() - t0
+    oracle.set_threads(cores)
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -621,6 +671,8 @@ def cpu_baseline(torch, si, b, y_dev, R, B_step, repeats):
             "sample": "the full prefill workload (8192 tokens, 65536 "
                       "assignments): layout + scatter_quant + combine, "
                       "median of %d runs, %.2f s each" % (repeats, t),
+            "single_thread": {"value": round(B_step / t1 / 1e9, 3),
+                              "seconds": round(t1, 2)},
             "cpu_model": cpu_model}
 
 
