@@ -67,12 +67,57 @@ __device__ __forceinline__ bool fast_scale(float b) {
   return !(__builtin_fabsf(b) < 0x1p-90f);  // NaN takes the fast path too
 }
 
-// Sixteen e4m3 bytes times b -> sixteen bf16 (o0: channels 0-7, o1: 8-15).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 (nearest even) with v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const bf16x2_t h = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Nonzero when some byte of w is an e4m3 NaN (S.1111.111).
+__device__ __forceinline__ uint32_t nan_byte_bits(uint32_t w) {
+  const uint32_t x = ~(w | 0x80808080u);  // a NaN byte becomes 0x00
+  return (x - 0x01010101u) & ~x & 0x80808080u;
+}
+
+// Sixteen e4m3 bytes times b -> sixteen bf16 (o0: channels 0-7, o1: 8-15),
+// each the exactly rounded product.  Fast path: the fp32 product rounded by
+// v_cvt_pk_bf16_f32.  That equals the exact rounding unless the fp32 product
+// sits exactly on a bf16 rounding midpoint (low 16 bits 0x8000, about one
+// product in 65536), so a lane holding such a product, an unusual scale
+// (below 2^-90 or not finite) or, when CHECK_NAN, a NaN byte recomputes its
+// sixteen products with the exact routines above.
+template <bool CHECK_NAN>
 __device__ __forceinline__ void upscale16(const u32x4& v, float b, u32x4& o0,
                                           u32x4& o1) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float p[16];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+    const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+    p[4 * k] = f01[0] * b;
+    p[4 * k + 1] = f01[1] * b;
+    p[4 * k + 2] = f23[0] * b;
+    p[4 * k + 3] = f23[1] * b;
+  }
+  // zero exactly when some product's low 16 bits are 0x8000
+  uint32_t mid = 0xFFFFu;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    mid = min(mid, (__float_as_uint(p[k]) ^ 0x8000u) & 0xFFFFu);
+  bool slow = !fast_scale(b) | (mid == 0u);  // this lane takes the exact path
+  if (CHECK_NAN)
+    slow = slow | !__builtin_isfinite(b) |
+           ((nan_byte_bits(w[0]) | nan_byte_bits(w[1]) | nan_byte_bits(w[2]) |
+             nan_byte_bits(w[3])) != 0u);
   uint32_t r[8];
-  if (fast_scale(b)) {
+  if (!slow) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = cvt_pk_bf16(p[2 * k], p[2 * k + 1]);
+  } else if (fast_scale(b)) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
@@ -109,7 +154,7 @@ __global__ __launch_bounds__(1024) void upscale_kernel(
     const u32x4 v = load16(qr + col);
     const float b = sr[(int64_t)(col / G) * s_cs];
     u32x4 o0, o1;
-    upscale16(v, b, o0, o1);
+    upscale16<true>(v, b, o0, o1);
     store16(orow + col, o0);
     store16(orow + col + 8, o1);
   }
@@ -142,7 +187,7 @@ __global__ __launch_bounds__(kWThreads) void weight_requant_kernel(
     const int32_t rr = r0 + (k >> 3), cc = c0 + (k & 7) * 16;
     if (rr < N && cc < K) {
       const u32x4 v = load16(qb + (int64_t)rr * ld + cc);
-      upscale16(v, si, w0[u], w1[u]);
+      upscale16<false>(v, si, w0[u], w1[u]);
       m = max(m, max(max(bf16x2_absmax_bits(w0[u].x), bf16x2_absmax_bits(w0[u].y)),
                      max(bf16x2_absmax_bits(w0[u].z), bf16x2_absmax_bits(w0[u].w))));
       m = max(m, max(max(bf16x2_absmax_bits(w1[u].x), bf16x2_absmax_bits(w1[u].y)),
