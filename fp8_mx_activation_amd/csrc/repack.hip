@@ -12,16 +12,16 @@
 //                              flag instead of being truncated silently;
 //   moe_masked_slab_to_expand  slab -> expanded rows with the top-k weight
 //                              applied on real rows only.
-// All grids depend only on host arguments (E, max_m, num_rows), so every
-// call can be captured in a hipGraph.
+// The copies launch blocks per (expert, range of slab rows); a block deals
+// its rows' 16-byte vectors to its threads and issues a round of loads
+// before the stores.  All grids depend only on host arguments, so every call
+// can be captured in a hipGraph.
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
 
 namespace {
 
 using namespace mxq;
-
-constexpr int kRowsPerBlock = 8;
 
 __device__ __forceinline__ int64_t psum_start(const int32_t* psum, int e,
                                               int32_t align) {
@@ -63,55 +63,89 @@ __global__ __launch_bounds__(1024) void m_indices_from_psum_kernel(
   }
 }
 
-// Block (e, b) copies rows [b*kRowsPerBlock, (b+1)*kRowsPerBlock) of expert
-// e's slab.  Row payloads move as 16-byte vectors, scale entries one by one
-// through their strides.
-__global__ __launch_bounds__(256) void expand_to_slab_kernel(
+constexpr int kCopyThreads = 1024;
+constexpr int kVecPerThread = 8;  // 16-byte loads in flight per thread
+
+// Rows per block of the copy kernels: at least 8, and at most 64 blocks per
+// expert, so the grid stays bounded for large slab capacities.
+inline int64_t copy_rows_per_block(int32_t max_m) {
+  const int64_t r = ceil_div(max_m, 64);
+  return r < 8 ? 8 : r;
+}
+
+// Block (e, b) copies rows [b*rpb, (b+1)*rpb) of expert e's slab, limited to
+// the rows that exist.  The rows' 16-byte vectors are numbered and dealt
+// round-robin to the threads; each thread issues up to kVecPerThread loads
+// before its stores, so a block costs about one memory round trip.
+// Block 0 also writes masked_m and the flags for every expert.
+__global__ __launch_bounds__(kCopyThreads) void expand_to_slab_kernel(
     const uint8_t* __restrict__ x, int64_t ld_x, int64_t src_rows,
     int64_t row_bytes, const uint8_t* __restrict__ xs, int64_t xs_rs,
     int64_t xs_cs, int32_t s_cols, int32_t s_elem,
     const int32_t* __restrict__ psum, int32_t E, int32_t align, int32_t max_m,
-    uint8_t* __restrict__ slab, int64_t ld_slab, uint8_t* __restrict__ ss,
-    int64_t ss_rs, int64_t ss_cs, int32_t* __restrict__ masked_m,
-    int32_t* __restrict__ flags) {
-  const int e = blockIdx.x / ((max_m + kRowsPerBlock - 1) / kRowsPerBlock);
-  const int b = blockIdx.x % ((max_m + kRowsPerBlock - 1) / kRowsPerBlock);
-  const int64_t s = psum_start(psum, e, align);
-  int64_t c = psum_count(psum, e, align);
-  if (c > max_m) c = max_m;
-  if (s + c > src_rows) c = src_rows > s ? src_rows - s : 0;
-  if (b == 0 && threadIdx.x == 0) masked_m[e] = (int32_t)c;
-  if (blockIdx.x == 0) {  // one writer for the flags word
+    int32_t rpb, uint8_t* __restrict__ slab, int64_t ld_slab,
+    uint8_t* __restrict__ ss, int64_t ss_rs, int64_t ss_cs,
+    int32_t* __restrict__ masked_m, int32_t* __restrict__ flags) {
+  const int nb = (max_m + rpb - 1) / rpb;
+  const int e = blockIdx.x / nb;
+  const int b = blockIdx.x % nb;
+  if (blockIdx.x == 0) {  // one writer for masked_m and the flags word
     int f = 0;
     for (int ee = threadIdx.x; ee < E; ee += blockDim.x) {
       const int64_t s2 = psum_start(psum, ee, align);
       int64_t c2 = psum_count(psum, ee, align);
       if (c2 > max_m) { f |= 1; c2 = max_m; }
-      if (s2 + c2 > src_rows) f |= 2;
+      if (s2 + c2 > src_rows) {
+        f |= 2;
+        c2 = src_rows > s2 ? src_rows - s2 : 0;
+      }
+      masked_m[ee] = (int32_t)c2;
     }
     const int any1 = __syncthreads_or(f & 1);
     const int any2 = __syncthreads_or(f & 2);
     if (threadIdx.x == 0) *flags = (any1 ? 1 : 0) | (any2 ? 2 : 0);
   }
-  const int64_t j0 = (int64_t)b * kRowsPerBlock;
-  const int64_t j1 = min(j0 + kRowsPerBlock, c);
-  const int64_t nvec = row_bytes / 16;
-  for (int64_t j = j0; j < j1; ++j) {
-    const uint8_t* src = x + (s + j) * ld_x;
-    uint8_t* dst = slab + ((int64_t)e * max_m + j) * ld_slab;
-    for (int64_t v = threadIdx.x; v < nvec; v += blockDim.x)
-      store16(dst + v * 16, load16(src + v * 16));
-    if (xs != nullptr) {
-      const uint8_t* srs = xs + (s + j) * xs_rs;
-      uint8_t* drs = ss + ((int64_t)e * max_m + j) * ss_rs;
-      for (int g = threadIdx.x; g < s_cols; g += blockDim.x) {
-        if (s_elem == 4) {
-          uint32_t w;
-          __builtin_memcpy(&w, srs + g * xs_cs, 4);
-          __builtin_memcpy(drs + g * ss_cs, &w, 4);
-        } else {
-          drs[g * ss_cs] = srs[g * xs_cs];
-        }
+  const int64_t s = psum_start(psum, e, align);
+  int64_t c = psum_count(psum, e, align);
+  if (c > max_m) c = max_m;
+  if (s + c > src_rows) c = src_rows > s ? src_rows - s : 0;
+  const int64_t j0 = (int64_t)b * rpb;
+  const int64_t nrows = min(j0 + rpb, c) - j0;
+  if (nrows <= 0) return;
+  // a block's items fit in 32 bits (checked on the host)
+  const uint32_t nvec = (uint32_t)(row_bytes / 16);
+  const uint32_t items = (uint32_t)nrows * nvec;
+  const uint32_t per_round = blockDim.x * kVecPerThread;
+  const uint8_t* src0 = x + (s + j0) * ld_x;
+  uint8_t* dst0 = slab + ((int64_t)e * max_m + j0) * ld_slab;
+  for (uint32_t base = 0; base < items; base += per_round) {
+    u32x4 v[kVecPerThread];
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const uint32_t i = base + u * blockDim.x + threadIdx.x;
+      if (i < items)
+        v[u] = load16(src0 + (int64_t)(i / nvec) * ld_x + (i % nvec) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const uint32_t i = base + u * blockDim.x + threadIdx.x;
+      if (i < items)
+        store16(dst0 + (int64_t)(i / nvec) * ld_slab + (i % nvec) * 16, v[u]);
+    }
+  }
+  if (xs != nullptr && s_cols > 0) {
+    const uint32_t sitems = (uint32_t)nrows * (uint32_t)s_cols;
+    for (uint32_t i = threadIdx.x; i < sitems; i += blockDim.x) {
+      const int64_t j = j0 + i / (uint32_t)s_cols;
+      const int64_t g = i % (uint32_t)s_cols;
+      const uint8_t* sp = xs + (s + j) * xs_rs + g * xs_cs;
+      uint8_t* dp = ss + ((int64_t)e * max_m + j) * ss_rs + g * ss_cs;
+      if (s_elem == 4) {
+        uint32_t w;
+        __builtin_memcpy(&w, sp, 4);
+        __builtin_memcpy(dp, &w, 4);
+      } else {
+        *dp = *sp;
       }
     }
   }
@@ -124,33 +158,56 @@ __device__ __forceinline__ uint32_t scale_bf16x2(uint32_t v, float w) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
+// Block (e, b) writes expanded rows start_e + j for j in [b*rpb,
+// (b+1)*rpb), j < min(masked_m[e], max_m) and start_e + j < out_rows, from
+// slab row e*max_m + j, times w[start_e + j] when weighted; loads issued a
+// round at a time as in expand_to_slab_kernel.
 template <bool WEIGHTED>
-__global__ __launch_bounds__(256) void slab_to_expand_kernel(
+__global__ __launch_bounds__(kCopyThreads) void slab_to_expand_kernel(
     const uint16_t* __restrict__ slab, int64_t ld_slab, int32_t H,
     const int32_t* __restrict__ masked_m, const int32_t* __restrict__ psum,
-    int32_t align, int32_t max_m, const float* __restrict__ w,
+    int32_t align, int32_t max_m, int32_t rpb, const float* __restrict__ w,
     uint16_t* __restrict__ out, int64_t ld_out, int64_t out_rows) {
-  const int nb = (max_m + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int nb = (max_m + rpb - 1) / rpb;
   const int e = blockIdx.x / nb;
   const int b = blockIdx.x % nb;
   const int64_t s = psum_start(psum, e, align);
   int64_t c = masked_m[e];
   if (c > max_m) c = max_m;
-  const int64_t j0 = (int64_t)b * kRowsPerBlock;
-  const int64_t j1 = min(j0 + kRowsPerBlock, c);
-  for (int64_t j = j0; j < j1 && s + j < out_rows; ++j) {
-    const uint16_t* src = slab + ((int64_t)e * max_m + j) * ld_slab;
-    uint16_t* dst = out + (s + j) * ld_out;
-    const float wj = WEIGHTED ? w[s + j] : 1.0f;
-    for (int col = threadIdx.x * 8; col < H; col += blockDim.x * 8) {
-      u32x4 v = load16(src + col);
-      if (WEIGHTED) {
-        v.x = scale_bf16x2(v.x, wj);
-        v.y = scale_bf16x2(v.y, wj);
-        v.z = scale_bf16x2(v.z, wj);
-        v.w = scale_bf16x2(v.w, wj);
+  if (s + c > out_rows) c = out_rows > s ? out_rows - s : 0;
+  const int64_t j0 = (int64_t)b * rpb;
+  const int64_t nrows = min(j0 + rpb, c) - j0;
+  if (nrows <= 0) return;
+  // a block's items fit in 32 bits (checked on the host)
+  const uint32_t nvec = (uint32_t)H / 8;
+  const uint32_t items = (uint32_t)nrows * nvec;
+  const uint32_t per_round = blockDim.x * kVecPerThread;
+  const uint16_t* src0 = slab + ((int64_t)e * max_m + j0) * ld_slab;
+  uint16_t* dst0 = out + (s + j0) * ld_out;
+  for (uint32_t base = 0; base < items; base += per_round) {
+    u32x4 v[kVecPerThread];
+    float wv[kVecPerThread];
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const uint32_t i = base + u * blockDim.x + threadIdx.x;
+      if (i < items) {
+        v[u] = load16(src0 + (int64_t)(i / nvec) * ld_slab + (i % nvec) * 8);
+        wv[u] = WEIGHTED ? w[s + j0 + i / nvec] : 1.0f;
       }
-      store16(dst + col, v);
+    }
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const uint32_t i = base + u * blockDim.x + threadIdx.x;
+      if (i < items) {
+        u32x4 o = v[u];
+        if (WEIGHTED) {
+          o.x = scale_bf16x2(o.x, wv[u]);
+          o.y = scale_bf16x2(o.y, wv[u]);
+          o.z = scale_bf16x2(o.z, wv[u]);
+          o.w = scale_bf16x2(o.w, wv[u]);
+        }
+        store16(dst0 + (int64_t)(i / nvec) * ld_out + (i % nvec) * 8, o);
+      }
     }
   }
 }
@@ -203,12 +260,16 @@ extern "C" mxq_status moe_expand_to_masked_slab(
          (xs_row_stride | xs_col_stride | ss_row_stride | ss_col_stride) % 4))
       return MXQ_ERR_INVALID_ARGUMENT;
   }
-  const int64_t blocks = (int64_t)E * ceil_div(max_m, kRowsPerBlock);
-  if (blocks > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
-  expand_to_slab_kernel<<<(unsigned)blocks, 256, 0, as_stream(stream)>>>(
+  const int64_t rpb = copy_rows_per_block(max_m);
+  const int64_t blocks = (int64_t)E * ceil_div(max_m, rpb);
+  if (blocks > INT32_MAX ||
+      rpb * (row_bytes / 16 + scale_cols) > (int64_t)INT32_MAX / 2)
+    return MXQ_ERR_UNSUPPORTED;
+  expand_to_slab_kernel<<<(unsigned)blocks, kCopyThreads, 0,
+                          as_stream(stream)>>>(
       static_cast<const uint8_t*>(x), ld_x, src_rows, row_bytes,
       static_cast<const uint8_t*>(x_scales), xs_row_stride, xs_col_stride,
-      scale_cols, scale_elem_bytes, psum, E, align, max_m,
+      scale_cols, scale_elem_bytes, psum, E, align, max_m, (int32_t)rpb,
       static_cast<uint8_t*>(slab), ld_slab, static_cast<uint8_t*>(slab_scales),
       ss_row_stride, ss_col_stride, masked_m, flags);
   return launch_status();
@@ -229,17 +290,21 @@ extern "C" mxq_status moe_masked_slab_to_expand(
   if (!aligned16(slab_bf16) || (ld_slab * 2) % 16 != 0 || ld_slab < H ||
       !aligned16(out_bf16) || (ld_out * 2) % 16 != 0 || ld_out < H)
     return MXQ_ERR_INVALID_ARGUMENT;
-  const int64_t blocks = (int64_t)E * ceil_div(max_m, kRowsPerBlock);
-  if (blocks > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
+  const int64_t rpb = copy_rows_per_block(max_m);
+  const int64_t blocks = (int64_t)E * ceil_div(max_m, rpb);
+  if (blocks > INT32_MAX || rpb * (H / 8) > (int64_t)INT32_MAX / 2)
+    return MXQ_ERR_UNSUPPORTED;
   const uint16_t* sl = static_cast<const uint16_t*>(slab_bf16);
   uint16_t* o = static_cast<uint16_t*>(out_bf16);
   if (weights != nullptr)
-    slab_to_expand_kernel<true><<<(unsigned)blocks, 256, 0, as_stream(stream)>>>(
-        sl, ld_slab, H, masked_m, psum, align, max_m, weights, o, ld_out,
-        out_rows);
+    slab_to_expand_kernel<true><<<(unsigned)blocks, kCopyThreads, 0,
+                                  as_stream(stream)>>>(
+        sl, ld_slab, H, masked_m, psum, align, max_m, (int32_t)rpb, weights,
+        o, ld_out, out_rows);
   else
-    slab_to_expand_kernel<false><<<(unsigned)blocks, 256, 0, as_stream(stream)>>>(
-        sl, ld_slab, H, masked_m, psum, align, max_m, nullptr, o, ld_out,
-        out_rows);
+    slab_to_expand_kernel<false><<<(unsigned)blocks, kCopyThreads, 0,
+                                   as_stream(stream)>>>(
+        sl, ld_slab, H, masked_m, psum, align, max_m, (int32_t)rpb, nullptr,
+        o, ld_out, out_rows);
   return launch_status();
 }

@@ -304,6 +304,9 @@ mxq_status moe_expand_to_masked_slab(
  * and start_e + j < out_rows: out[start_e + j] = bf16(w[start_e + j] *
  * slab[e*max_m + j]) (fp32 product, one nearest-even rounding), or a plain
  * copy when weights is NULL.  Every other output row is left untouched.
+ * masked_m[e] must not reach past the expert's region (start_{e+1} -
+ * start_e rows), which holds for the values moe_expand_to_masked_slab
+ * writes; a larger value gives unspecified but in-bounds results.
  *   slab_bf16 [E * max_m, ld_slab], out_bf16 [out_rows, ld_out] (elements),
  *   weights fp32 [out_rows] or NULL; H % 8 == 0. */
 mxq_status moe_masked_slab_to_expand(
