@@ -139,3 +139,113 @@ def test_graph_replay_full_path(ora):
                      "psum m_indices")
         # eager work between replays
         _ = (x_s.float() * 2).sum().item()
+
+
+def test_graph_replay_variants_upscale_weights(ora):
+    """The scale variants, the upscale, the weight requant and a two-launch
+    layout (T*K > 8192) captured once and replayed three times with new
+    inputs and eager work between replays; every replay is checked."""
+    T, H, E, K, G = 1100, 256, 40, 8, 32
+    R = ora.compact_row_bound(T * K, E, 128)
+    ng = H // G
+    ids_s = torch.zeros((T, K), dtype=torch.int32, device=DEV)
+    x_s = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
+    lay_out = {k: torch.empty(shape, dtype=torch.int32, device=DEV)
+               for k, shape in (("counts", (E,)), ("expert_offsets", (E + 1,)),
+                                ("m_indices", (R,)), ("masked_m", (E,)),
+                                ("src2dst", (T, K)), ("overflow_flag", (1,)))}
+    ws = torch.empty(max(1, mxq.moe_layout_workspace_bytes(T, K, E)),
+                     dtype=torch.uint8, device=DEV)
+    q_s = torch.empty((R, H), dtype=torch.uint8, device=DEV)
+    pk_s = mxq.packed_mn_scales(R, ng, DEV)
+    live_s = torch.zeros(4, dtype=torch.int32, device=DEV)
+    ql_s = torch.empty((T, H), dtype=torch.uint8, device=DEV)
+    sl_s = torch.empty((T, ng), dtype=torch.uint8, device=DEV)
+    uq_s = torch.zeros((T, H), dtype=torch.uint8, device=DEV)
+    us_s = torch.ones((T, H // 128), dtype=torch.float32, device=DEV)
+    uo_s = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    wq_s = torch.zeros((2, 256, 384), dtype=torch.uint8, device=DEV)
+    wsi_s = torch.ones((2, 2, 3), dtype=torch.float32, device=DEV)
+    wo_s = torch.empty_like(wq_s)
+    wso_s = torch.empty((2, 2, 3), dtype=torch.uint8, device=DEV)
+
+    def step():
+        lay = mxq.moe_layout(ids_s, 0, E, "compact", num_rows=R, out=lay_out,
+                             workspace=ws)
+        mxq.moe_scatter_quant_ex(x_s, lay["src2dst"], R, "e8m0_g32",
+                                 "ocp_floor", "packed_mn", q=q_s,
+                                 scales=pk_s)
+        mxq.mx_quant_live_rows_ex(x_s[:1100 // 4 * 4], 4, live_s,
+                                  "e8m0_g32", "ocp_floor", "rows",
+                                  q=ql_s[:1100 // 4 * 4],
+                                  scales=sl_s[:1100 // 4 * 4])
+        mxq.upscale_fp8_to_bf16(uq_s, us_s, T - 7, out=uo_s)
+        mxq.requant_weight_block_ue8m0(wq_s, wsi_s, q_out=wo_s,
+                                       scales_out=wso_s)
+
+    say("graph variants: warm-up on a side stream")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("graph variants: capture")
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        rng = np.random.default_rng(2000 + rep)
+        ids = si.zipf_topk(rng, T, E, K, n_zero=3)
+        x = si.gaussian_bf16(rng, (T, H))
+        live = np.array([rep * 37 % 275, 275, 0, 100 + rep], np.int32)
+        uq = si.random_e4m3_bytes(rng, (T, H))
+        usc = si.group_scales_f32(rng, (T, H // 128))
+        wq, wsi = si.block_weights(3000 + rep, 2, 256, 384)
+        ids_s.copy_(i32_to_dev(ids))
+        x_s.copy_(bf16_to_dev(x))
+        live_s.copy_(i32_to_dev(live))
+        uq_s.copy_(u8_to_dev(uq))
+        us_s.copy_(f32_to_dev(usc))
+        wq_s.copy_(u8_to_dev(wq))
+        wsi_s.copy_(f32_to_dev(wsi))
+        q_s.fill_(0xA5)
+        pk_s.fill_(-1)
+        ql_s.fill_(0xA5)
+        sl_s.fill_(0xA5)
+        uo_s.view(torch.int16).fill_(0x1234)
+        torch.cuda.synchronize()
+        say("graph variants: replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+
+        ref = ora.moe_layout(ids, 0, E, "compact", num_rows=R)
+        assert_equal(host(lay_out["src2dst"]), ref["src2dst"], "src2dst")
+        q_ref, pk_ref = ora.scatter_quant_ex(
+            x, ref["src2dst"], G, R, "ocp_floor", "packed_mn",
+            q=np.full((R, H), 0xA5, np.uint8),
+            s=np.full(pk_s.shape, 0xFFFFFFFF, np.uint32))
+        assert_equal(host(q_s), q_ref, "scatter_ex fp8")
+        assert_equal(host(pk_s).view(np.uint32), pk_ref, "packed scales")
+        n4 = 1100 // 4 * 4
+        d = np.full((n4, 1), -1, np.int32)
+        rps = n4 // 4
+        for gi in range(4):
+            nl = min(int(live[gi]), rps)
+            d[gi * rps:gi * rps + nl, 0] = np.arange(gi * rps, gi * rps + nl)
+        ql_ref, sl_ref = ora.scatter_quant_ex(
+            x[:n4], d, G, n4, "ocp_floor", "rows",
+            q=np.full((n4, H), 0xA5, np.uint8),
+            s=np.full((n4, ng), 0xA5, np.uint8))
+        assert_equal(host(ql_s)[:n4], ql_ref, "live_ex fp8")
+        assert_equal(host(sl_s)[:n4], sl_ref, "live_ex scales")
+        uo_ref = ora.upscale_fp8(uq, usc, num_rows=T - 7,
+                                 out=np.full((T, H), 0x1234, np.uint16))
+        assert_equal(bf16_to_host(uo_s), uo_ref, "upscale")
+        wo_ref, wso_ref = ora.requant_weight_block_ue8m0(wq, wsi)
+        assert_equal(host(wo_s), wo_ref, "weights")
+        assert_equal(host(wso_s), wso_ref, "weight scales")
+        # eager work between replays
+        _ = (x_s.float() * 2).sum().item()
