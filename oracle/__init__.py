@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
             "ora_masked_slab_to_expand": (
                 None, [_p, _i64, _i32, _p, _p, _i32, _i32, _i32, _p, _p, _i64,
                        _i64]),
+            "ora_scatter_rows": (None, [_p, _i64, _i64, _i64, _p, _i64, _i64,
+                                        _i32, _i32, _p, _i32, _i64, _p, _i64,
+                                        _p, _i64, _i64]),
             "ora_bf16_round_f64": (ctypes.c_uint16, [ctypes.c_double]),
             "ora_bf16_round_f64_array": (None, [_p, _i64, _p]),
             "ora_upscale_fp8": (None, [_p, _i64, _p, _i64, _i64, _i64, _i32,
@@ -399,6 +402,43 @@ def masked_slab_to_expand(slab_bf16: np.ndarray, masked_m, psum, align: int,
                                     align, max_m, 0 if w is None else _ptr(w),
                                     _ptr(out), out.shape[1], out.shape[0])
     return out
+
+
+# ------------------------------------------------ scatter of quantized rows
+
+def scatter_rows(x_rows, src2dst, num_rows: int, scales=None,
+                 scales_col_major: bool = False, out=None, out_scales=None,
+                 out_scales_col_major: bool = False):
+    """x_rows: uint8 [T, row_bytes] payload; scales: [T, cols] (or [cols, T]
+    with scales_col_major) of 1- or 4-byte entries.  out / out_scales (same
+    entry type, [num_rows, cols] or [cols, num_rows]) are updated in place on
+    destination rows only."""
+    x = _c(x_rows, np.uint8)
+    T, rb = x.shape
+    d = _c(src2dst, np.int32)
+    K = d.shape[1] if d.ndim == 2 else 1
+    if out is None:
+        out = np.zeros((num_rows, rb), np.uint8)
+    assert out.flags.c_contiguous and out.dtype == np.uint8
+    xs_p, xs_rs, xs_cs, cols, elem = 0, 0, 0, 0, 1
+    os_p, os_rs, os_cs = 0, 0, 0
+    if scales is not None:
+        sc = np.ascontiguousarray(scales)
+        elem = sc.dtype.itemsize
+        cols = sc.shape[0] if scales_col_major else sc.shape[1]
+        xs_rs, xs_cs = ((elem, elem * T) if scales_col_major
+                        else (elem * cols, elem))
+        if out_scales is None:
+            out_scales = np.zeros((cols, num_rows) if out_scales_col_major
+                                  else (num_rows, cols), sc.dtype)
+        assert out_scales.flags.c_contiguous
+        os_rs, os_cs = ((elem, elem * num_rows) if out_scales_col_major
+                        else (elem * cols, elem))
+        xs_p, os_p = _ptr(sc), _ptr(out_scales)
+    lib().ora_scatter_rows(_ptr(x), rb, T, rb, xs_p, xs_rs, xs_cs, cols, elem,
+                           _ptr(d), K, num_rows, _ptr(out), out.shape[1],
+                           os_p, os_rs, os_cs)
+    return out, out_scales
 
 
 # -------------------------------------------------------- receive-side upscale

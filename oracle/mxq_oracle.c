@@ -628,6 +628,34 @@ void ora_masked_slab_to_expand(const uint16_t* slab, int64_t ld_slab,
   }
 }
 
+/* ---------------------------------------------- scatter of quantized rows */
+
+/* Rows already quantized by the sender (fp8 payload plus scales) copied to
+ * their destination rows [P3 Implementation breakdown item 3 and the
+ * deep_gemm.py snippet: on the prefill path the dispatcher's rows are written
+ * into the contiguous layout at the offsets its psum gives, with the scales
+ * copied through their own strides].  For each (t, j) with 0 <= d =
+ * src2dst[t*K + j] < num_rows: row d of out takes row t of x (row_bytes
+ * bytes) and, if scales are given, scale entry (d, g) takes entry (t, g) for
+ * g < scale_cols (entries of elem bytes at row/column strides in bytes). */
+void ora_scatter_rows(const uint8_t* x, int64_t ld_x, int64_t T,
+                      int64_t row_bytes, const uint8_t* xs, int64_t xs_rs,
+                      int64_t xs_cs, int32_t scale_cols, int32_t elem,
+                      const int32_t* src2dst, int32_t K, int64_t num_rows,
+                      uint8_t* out, int64_t ld_out, uint8_t* os, int64_t os_rs,
+                      int64_t os_cs) {
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t j = 0; j < K; ++j) {
+      const int64_t d = src2dst[t * K + j];
+      if (d < 0 || d >= num_rows) continue;
+      memcpy(out + d * ld_out, x + t * ld_x, (size_t)row_bytes);
+      if (xs == NULL) continue;
+      for (int32_t g = 0; g < scale_cols; ++g)
+        memcpy(os + d * os_rs + (int64_t)g * os_cs,
+               xs + t * xs_rs + (int64_t)g * xs_cs, (size_t)elem);
+    }
+}
+
 /* ------------------------------------------------------ receive-side upscale */
 
 /* fp8 payload with group-G fp32 scales -> bf16, over the first `rows` rows
