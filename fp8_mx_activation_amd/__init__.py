@@ -28,7 +28,7 @@ __all__ = [
     "moe_scatter_quant_ex", "mx_quant_live_rows_ex", "packed_mn_scales",
     "requant_per_token_to_per_tensor", "moe_combine", "mxq_e4m3_encode_f32",
     "mxq_abi_version", "moe_m_indices_from_psum", "moe_expand_to_masked_slab",
-    "moe_masked_slab_to_expand", "upscale_fp8_to_bf16",
+    "moe_masked_slab_to_expand", "moe_scatter_rows", "upscale_fp8_to_bf16",
     "requant_weight_block_ue8m0",
 ]
 
@@ -74,6 +74,9 @@ _SIGNATURES = {
                                          _i64, _p, _i64, _i64, _p, _p, _p]),
     "moe_masked_slab_to_expand": (_i32, [_p, _i64, _i32, _p, _p, _i32, _i32,
                                          _i32, _p, _p, _i64, _i64, _p]),
+    "moe_scatter_rows": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _i64, _i32,
+                                _i32, _p, _i32, _i64, _p, _i64, _p, _i64,
+                                _i64, _p]),
     "upscale_fp8_to_bf16": (_i32, [_p, _i64, _p, _i64, _i64, _i64, _i32,
                                    _i32, _p, _i64, _p]),
     "requant_weight_block_ue8m0": (_i32, [_p, _i64, _i64, _p, _i64, _i64,
@@ -601,6 +604,77 @@ def moe_masked_slab_to_expand(slab: torch.Tensor, masked_m: torch.Tensor,
         max_m, _ptr(weights), _ptr(out), ld_out, out.shape[0], _stream(slab))
     _check("moe_masked_slab_to_expand", st)
     return out
+
+
+# ------------------------------------------------ scatter of quantized rows
+
+def _scale_strides(t: torch.Tensor, col_major: bool, rows: int, name: str):
+    """(row stride, column stride) in bytes and column count of a 2-D scale
+    tensor stored [rows, cols] or, when col_major, [cols, rows]."""
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    e = t.element_size()
+    if col_major:
+        cols = t.shape[0]
+        if t.shape[1] < rows or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError("%s must be [cols, >= %d] with unit row stride"
+                             % (name, rows))
+        return e, e * t.stride(0), cols
+    cols = t.shape[1]
+    if t.shape[0] < rows or (cols > 1 and t.stride(1) != 1):
+        raise ValueError("%s must be [>= %d, cols] with unit column stride"
+                         % (name, rows))
+    return e * t.stride(0), e, cols
+
+
+def moe_scatter_rows(x: torch.Tensor, src2dst: torch.Tensor, num_rows: int,
+                     scales: torch.Tensor | None = None,
+                     scales_col_major: bool = False,
+                     out: torch.Tensor | None = None,
+                     out_scales: torch.Tensor | None = None,
+                     out_scales_col_major: bool = False):
+    """Already-quantized rows (any 1-byte payload, e.g. fp8) and optional
+    scales (1- or 4-byte entries) copied to their destination rows in
+    ``src2dst``.  Returns ``(out, out_scales)``; rows that are no
+    destination keep the contents of a given ``out``."""
+    _dev(x, "x")
+    xx = _u8(x)
+    ld_x = _rows(xx, "x", (torch.uint8,))
+    T, rb = xx.shape
+    if src2dst.dtype != torch.int32 or src2dst.dim() != 2 or \
+            src2dst.shape[0] != T or not src2dst.is_contiguous():
+        raise ValueError("src2dst must be contiguous int32 [T, K]")
+    K = src2dst.shape[1]
+    if out is None:
+        out = _empty_rows_u8(num_rows, rb, x.device)
+    oo = _u8(out)
+    ld_o = _rows(oo, "out", (torch.uint8,))
+    if oo.shape[0] < num_rows or oo.shape[1] < rb:
+        raise ValueError("out must be at least [num_rows, row bytes]")
+    xs_rs = xs_cs = os_rs = os_cs = 0
+    cols, elem = 0, 1
+    if scales is not None:
+        _dev(scales, "scales")
+        elem = scales.element_size()
+        xs_rs, xs_cs, cols = _scale_strides(scales, scales_col_major, T,
+                                            "scales")
+        if out_scales is None:
+            shape = (cols, num_rows) if out_scales_col_major else \
+                (num_rows, cols)
+            out_scales = torch.empty(shape, dtype=scales.dtype,
+                                     device=x.device)
+        if out_scales.element_size() != elem:
+            raise TypeError("out_scales must have the scales' entry size")
+        os_rs, os_cs, ocols = _scale_strides(out_scales, out_scales_col_major,
+                                             num_rows, "out_scales")
+        if ocols < cols:
+            raise ValueError("out_scales has fewer columns than scales")
+    st = lib().moe_scatter_rows(_ptr(xx), ld_x, T, rb, _ptr(scales), xs_rs,
+                                xs_cs, cols, elem, _ptr(src2dst), K, num_rows,
+                                _ptr(oo), ld_o, _ptr(out_scales), os_rs,
+                                os_cs, _stream(x))
+    _check("moe_scatter_rows", st)
+    return out, out_scales
 
 
 # ---------------------------------------------------- receive-side upscale

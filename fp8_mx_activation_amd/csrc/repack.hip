@@ -11,7 +11,10 @@
 //                              plus masked_m; over-capacity experts raise a
 //                              flag instead of being truncated silently;
 //   moe_masked_slab_to_expand  slab -> expanded rows with the top-k weight
-//                              applied on real rows only.
+//                              applied on real rows only;
+//   moe_scatter_rows           the prefill path: a dispatcher's quantized
+//                              rows and scales written into the contiguous
+//                              layout (psum offsets) by src2dst.
 // The copies launch blocks per (expert, range of slab rows); a block deals
 // its rows' 16-byte vectors to its threads and issues a round of loads
 // before the stores.  All grids depend only on host arguments, so every call
@@ -212,7 +215,83 @@ __global__ __launch_bounds__(kCopyThreads) void slab_to_expand_kernel(
   }
 }
 
+// One block per token: each thread loads its 16-byte vectors of the row once
+// and stores them to every destination of the token (streaming stores);
+// scale entries are copied through their strides.
+__global__ __launch_bounds__(1024) void scatter_rows_kernel(
+    const uint8_t* __restrict__ x, int64_t ld_x, int64_t row_bytes,
+    const uint8_t* __restrict__ xs, int64_t xs_rs, int64_t xs_cs,
+    int32_t s_cols, int32_t s_elem, const int32_t* __restrict__ src2dst,
+    int32_t K, int64_t num_rows, uint8_t* __restrict__ out, int64_t ld_out,
+    uint8_t* __restrict__ os, int64_t os_rs, int64_t os_cs) {
+  const int64_t t = blockIdx.x;
+  const int32_t* dl = src2dst + t * K;
+  const uint8_t* src = x + t * ld_x;
+  const int64_t nvec = row_bytes / 16;
+  for (int64_t v = threadIdx.x; v < nvec; v += blockDim.x) {
+    const u32x4 val = load16(src + v * 16);
+    for (int j = 0; j < K; ++j) {
+      const int64_t d = dl[j];
+      if (d >= 0 && d < num_rows) store16_nt(out + d * ld_out + v * 16, val);
+    }
+  }
+  if (xs == nullptr) return;
+  for (int g = threadIdx.x; g < s_cols; g += blockDim.x) {
+    const uint8_t* sp = xs + t * xs_rs + (int64_t)g * xs_cs;
+    uint32_t w = 0;
+    if (s_elem == 4)
+      __builtin_memcpy(&w, sp, 4);
+    else
+      w = *sp;
+    for (int j = 0; j < K; ++j) {
+      const int64_t d = dl[j];
+      if (d < 0 || d >= num_rows) continue;
+      uint8_t* dp = os + d * os_rs + (int64_t)g * os_cs;
+      if (s_elem == 4)
+        __builtin_memcpy(dp, &w, 4);
+      else
+        *dp = (uint8_t)w;
+    }
+  }
+}
+
 }  // namespace
+
+extern "C" mxq_status moe_scatter_rows(
+    const void* x, int64_t ld_x, int64_t T, int64_t row_bytes,
+    const void* x_scales, int64_t xs_row_stride, int64_t xs_col_stride,
+    int32_t scale_cols, int32_t scale_elem_bytes, const int32_t* src2dst,
+    int32_t K, int64_t num_rows, void* out, int64_t ld_out, void* out_scales,
+    int64_t os_row_stride, int64_t os_col_stride, void* stream) {
+  if (T < 0 || T > INT32_MAX || K < 0 || K > MXQ_MAX_TOPK || row_bytes < 0 ||
+      num_rows < 0)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (row_bytes % 16 != 0) return MXQ_ERR_UNSUPPORTED;
+  if (T == 0 || K == 0 || num_rows == 0) return MXQ_OK;
+  if (x == nullptr || src2dst == nullptr || out == nullptr)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || ld_x % 16 != 0 || ld_x < row_bytes ||
+      !aligned16(out) || ld_out % 16 != 0 || ld_out < row_bytes)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (x_scales != nullptr) {
+    if (out_scales == nullptr || scale_cols < 0 ||
+        (scale_elem_bytes != 1 && scale_elem_bytes != 4))
+      return MXQ_ERR_INVALID_ARGUMENT;
+    if (scale_elem_bytes == 4 &&
+        (((reinterpret_cast<uintptr_t>(x_scales) |
+           reinterpret_cast<uintptr_t>(out_scales)) & 3) != 0 ||
+         (xs_row_stride | xs_col_stride | os_row_stride | os_col_stride) % 4))
+      return MXQ_ERR_INVALID_ARGUMENT;
+  }
+  const int threads = row_block_threads(row_bytes > 0 ? row_bytes : 16, 16);
+  scatter_rows_kernel<<<(unsigned)T, threads, 0, as_stream(stream)>>>(
+      static_cast<const uint8_t*>(x), ld_x, row_bytes,
+      static_cast<const uint8_t*>(x_scales), xs_row_stride, xs_col_stride,
+      scale_cols, scale_elem_bytes, src2dst, K, num_rows,
+      static_cast<uint8_t*>(out), ld_out, static_cast<uint8_t*>(out_scales),
+      os_row_stride, os_col_stride);
+  return launch_status();
+}
 
 extern "C" mxq_status moe_m_indices_from_psum(const int32_t* psum, int32_t E,
                                               int32_t align, int64_t num_rows,

@@ -365,6 +365,32 @@ mxq_status requant_weight_block_ue8m0(
     int32_t K, int32_t block_n, int32_t block_k, void* q_out,
     uint8_t* scales_out, int64_t o_ld, int64_t o_matrix_stride, void* stream);
 
+/* Already-quantized rows (and their scales) written to their destination
+ * rows [P3 impl. item 3 and the deep_gemm.py snippet: on the prefill path
+ * the dispatcher's fp8 rows go into the contiguous layout at its psum
+ * offsets, scales copied through their own strides].  The psum geometry is
+ * the compact layout's (regions start at align(psum[e-1])), so moe_layout
+ * with block_e = the alignment gives the destinations in src2dst.
+ *
+ *   x            T rows of row_bytes bytes (row_bytes % 16 == 0), row stride
+ *                ld_x bytes, 16-byte aligned.
+ *   x_scales     optional: scale_cols entries of scale_elem_bytes (1 or 4)
+ *                per row, entry (t, g) at t*xs_row_stride + g*xs_col_stride
+ *                bytes; out_scales entry (d, g) at d*os_row_stride +
+ *                g*os_col_stride bytes (row- or column-major alike).
+ *   src2dst      int32 [T, K]; entries outside [0, num_rows) are skipped.
+ *   out          num_rows rows, stride ld_out bytes (% 16), 16-byte aligned.
+ * For each (t, j) with a valid destination d, row d of out (and its scale
+ * entries) takes row t of x.  Rows that are no destination are untouched. */
+mxq_status moe_scatter_rows(const void* x, int64_t ld_x, int64_t T,
+                            int64_t row_bytes, const void* x_scales,
+                            int64_t xs_row_stride, int64_t xs_col_stride,
+                            int32_t scale_cols, int32_t scale_elem_bytes,
+                            const int32_t* src2dst, int32_t K,
+                            int64_t num_rows, void* out, int64_t ld_out,
+                            void* out_scales, int64_t os_row_stride,
+                            int64_t os_col_stride, void* stream);
+
 /* ---------------------------------------------------------- diagnostics */
 
 /* The fp32 -> e4m3fn conversion every kernel above uses, exposed so it can

@@ -182,6 +182,29 @@ def test_upscale_and_weight_requant_validation(mxq):
     assert wr(B=0, q=None, s=None, qo=None, so=None) == 0
 
 
+def test_scatter_rows_validation(mxq):
+    L = mxq.lib()
+
+    def call(x=FAKE, ld_x=448, T=4, rb=448, xs=None, xrs=0, xcs=0, cols=0,
+             elem=1, s2d=FAKE, K=2, rows=16, out=FAKE, ld_o=448, os=None,
+             ors=0, ocs=0):
+        return L.moe_scatter_rows(x, ld_x, T, rb, xs, xrs, xcs, cols, elem,
+                                  s2d, K, rows, out, ld_o, os, ors, ocs, None)
+
+    assert call(rb=440, ld_x=448) == UNSUPPORTED   # row bytes % 16
+    assert call(K=65) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(ld_x=432) == INVALID               # stride < row
+    assert call(ld_o=456) == INVALID               # stride % 16
+    assert call(x=FAKE + 4) == INVALID
+    assert call(s2d=None) == INVALID
+    assert call(xs=FAKE, os=None) == INVALID
+    assert call(xs=FAKE, os=FAKE, cols=7, elem=2) == INVALID
+    assert call(xs=FAKE, os=FAKE, cols=7, elem=4, xrs=30) == INVALID
+    assert call(T=0, x=None, out=None) == 0
+    assert call(rows=0, out=None) == 0
+
+
 def test_layout_validation(mxq):
     L = mxq.lib()
 
