@@ -344,15 +344,18 @@ def main():
             "traffic": traffic,
         },
     }
-    variants = None
+    variants = srows = None
     if not args.no_rows:
         variants = scale_variant_rows(torch, mxq, x, lay_out["src2dst"], R,
                                       H, q, B_sq, dev)
+        srows = scatter_rows_row(torch, mxq, x, lay_out["src2dst"], R, H, q,
+                                 T, K, A, dev)
     del q, s, out
 
     if not args.no_rows:
         result["rows"] = other_rows(torch, mxq, si, dev)
         result["rows"]["scale_variants"] = variants
+        result["rows"]["scatter_rows"] = srows
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, si, b, y, R, B_step,
@@ -445,6 +448,22 @@ def scale_variant_rows(torch, mxq, x, src2dst, R, H, q, B_sq, dev):
             out["%s/%s_gbs" % (rule, layout)] = round(
                 B_sq / (us * 1e-6) / 1e9, 2)
     return out
+
+
+def scatter_rows_row(torch, mxq, x, src2dst, R, H, q, T, K, A, dev):
+    """The psum prefill path: the same tokens already quantized by the
+    sender (fp8 rows + 56 UE8M0 bytes) copied into the compact layout."""
+    q_tok, s_tok = mxq.mx_quant_live_rows(
+        x, 1, torch.tensor([T], dtype=torch.int32, device=dev),
+        fmt="ue8m0_g128")
+    so = torch.empty((R, H // 128), dtype=torch.uint8, device=dev)
+    us = time_calls(torch, lambda: mxq.moe_scatter_rows(
+        q_tok, src2dst, R, scales=s_tok, out=q, out_scales=so))
+    byts = T * (H + H // 128) + A * (H + H // 128) + T * K * 4
+    return {"workload": "prefill: 8192 fp8 token rows + 56 UE8M0 bytes "
+                        "-> 65536 rows of the 98048-row compact layout",
+            "us": round(us, 2), "algorithmic_bytes": byts,
+            "gbs": round(byts / (us * 1e-6) / 1e9, 2)}
 
 
 def other_rows(torch, mxq, si, dev):
