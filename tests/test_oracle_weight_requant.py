@@ -100,8 +100,8 @@ def test_error_bound_and_scale_minimality(ora):
                 blk = np.abs(w[b, i * 128:(i + 1) * 128, j * 128:(j + 1) * 128])
                 amax = blk.max() * (1 + 2.0 ** -8)
                 assert amax / 2.0 ** (ex - 1) > 448.0  # a smaller e clips
-                wb = np.abs(back[b, i * 128:(i + 1) * 128,
-                                 j * 128:(j + 1) * 128])
+                wb = (nearest_bf16(blk).astype(np.uint32) << 16).view(
+                    np.float32)
                 assert wb.max() <= 448.0 * 2.0 ** ex     # nothing clipped
                 assert (got_q[b, i * 128:(i + 1) * 128,
                               j * 128:(j + 1) * 128] & 0x7F).max() <= 0x7E
