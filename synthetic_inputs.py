@@ -100,6 +100,17 @@ def zipf_topk(rng: np.random.Generator, T: int, n_experts: int, K: int,
     return top.astype(np.int32)
 
 
+def strided_topk(rng: np.random.Generator, T: int, n_experts: int, K: int,
+                 stride: int = 131) -> np.ndarray:
+    """Top-K for very large T without a [T, n_experts] draw: a skewed base
+    expert b_t = floor(n_experts * u^3) per token, then experts (b_t + j *
+    stride) mod n_experts, distinct for j < K when stride * K stays below
+    n_experts or stride is odd and n_experts a power of two."""
+    b = np.floor(n_experts * rng.random(T) ** 3).astype(np.int64)
+    ids = (b[:, None] + np.arange(K, dtype=np.int64) * stride) % n_experts
+    return ids.astype(np.int32)
+
+
 def softmax_weights(rng: np.random.Generator, T: int, K: int) -> np.ndarray:
     """Routing weights: softmax over K standard-normal logits per token."""
     z = rng.standard_normal((T, K))
