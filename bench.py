@@ -354,6 +354,10 @@ def main():
 
     if not args.no_rows:
         result["rows"] = other_rows(torch, mxq, si, dev)
+        result["rows"]["timing"] = ("each row: GPU time per call, 20 calls "
+                                    "captured in a hipGraph, median of 5 "
+                                    "replays; cold variants flush the MALL "
+                                    "before each eager call")
         result["rows"]["scale_variants"] = variants
         result["rows"]["scatter_rows"] = srows
 
@@ -433,7 +437,8 @@ def scale_variant_rows(torch, mxq, x, src2dst, R, H, q, B_sq, dev):
     timed back to back (the plain entry point beside them, timed the same
     way)."""
     out = {"workload": "prefill scatter (8192 x 7168 -> 98048 rows, "
-                       "UE8M0 group-128), back-to-back calls",
+                       "UE8M0 group-128), back-to-back calls in a hipGraph "
+                       "(the 117 MB of token rows stay in the MALL)",
            "algorithmic_bytes": B_sq}
     s_rows = torch.empty((R, H // 128), dtype=torch.uint8, device=dev)
     s_mn = mxq.packed_mn_scales(R, H // 128, dev)
