@@ -121,13 +121,14 @@ __global__ __launch_bounds__(kCopyThreads) void expand_to_slab_kernel(
   const uint32_t per_round = blockDim.x * kVecPerThread;
   const uint8_t* src0 = x + (s + j0) * ld_x;
   uint8_t* dst0 = slab + ((int64_t)e * max_m + j0) * ld_slab;
+  // loads use an index clamped into range (no branch), so every load of a
+  // round is issued before the first wait; only the stores are guarded
   for (uint32_t base = 0; base < items; base += per_round) {
     u32x4 v[kVecPerThread];
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
-      const uint32_t i = base + u * blockDim.x + threadIdx.x;
-      if (i < items)
-        v[u] = load16(src0 + (int64_t)(i / nvec) * ld_x + (i % nvec) * 16);
+      const uint32_t i = min(base + u * blockDim.x + threadIdx.x, items - 1);
+      v[u] = load16(src0 + (int64_t)(i / nvec) * ld_x + (i % nvec) * 16);
     }
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
@@ -192,11 +193,9 @@ __global__ __launch_bounds__(kCopyThreads) void slab_to_expand_kernel(
     float wv[kVecPerThread];
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
-      const uint32_t i = base + u * blockDim.x + threadIdx.x;
-      if (i < items) {
-        v[u] = load16(src0 + (int64_t)(i / nvec) * ld_slab + (i % nvec) * 8);
-        wv[u] = WEIGHTED ? w[s + j0 + i / nvec] : 1.0f;
-      }
+      const uint32_t i = min(base + u * blockDim.x + threadIdx.x, items - 1);
+      v[u] = load16(src0 + (int64_t)(i / nvec) * ld_slab + (i % nvec) * 8);
+      wv[u] = WEIGHTED ? w[s + j0 + i / nvec] : 1.0f;
     }
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
