@@ -8,7 +8,7 @@
 // ascending flat assignment index t*K + j.
 //
 // Two launches whose grids depend only on T*K, E and num_rows (one launch,
-// the assign kernel in its SINGLE form, when T*K <= 8192):
+// the assign kernel in its SINGLE form, when T*K <= 4096):
 //   layout_hist_kernel    one block per chunk of assignments: LDS histogram
 //                         of the chunk's local experts -> cnt[chunk][E].
 //   layout_assign_kernel  one block of 16 wavefronts per chunk, plus enough
@@ -112,7 +112,7 @@ __device__ __forceinline__ void region_scan(
 // chunk base + count of the same expert in earlier wavefronts + its rank in
 // its wavefront: flat order, no atomics, no serial chain across wavefronts.
 //
-// SINGLE: all assignments form one chunk (T*K <= kChunkMax) and no
+// SINGLE: all assignments form one chunk (T*K <= kSingleMax) and no
 // histogram pass runs.  Every block ranks that chunk (C1), takes the totals
 // from the per-wavefront counts (C2) and then scans the regions (B); block 0
 // alone writes src2dst.
@@ -148,12 +148,19 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
   const int64_t w_begin = c_begin + (int64_t)wv * steps_per_wave * 64;
   const int64_t w_end = min(w_begin + (int64_t)steps_per_wave * 64, c_end);
 
-  // this wavefront's ids, fetched before anything waits
+  // this wavefront's ids, fetched before anything waits.  Each load reads
+  // an index clamped to the wavefront's last assignment (no branch, so all
+  // are in flight together; steps past the end re-read a line already
+  // fetched); which entries count is decided where they are used.
   int32_t idb[kMaxStepsPerWave];
+  if (A > 0) {
+    const int64_t a_last = w_end > w_begin ? w_end - 1 : A - 1;
 #pragma unroll
-  for (int st = 0; st < kMaxStepsPerWave; ++st) {
-    const int64_t a = w_begin + st * 64 + lane;
-    idb[st] = (st < steps_per_wave && a < w_end) ? ids[a] : 0;
+    for (int st = 0; st < kMaxStepsPerWave; ++st)
+      idb[st] = ids[min(w_begin + st * 64 + lane, a_last)];
+  } else {
+#pragma unroll
+    for (int st = 0; st < kMaxStepsPerWave; ++st) idb[st] = 0;
   }
 
   // A: totals and this chunk's first slots from the chunk counts.  Up to
@@ -369,7 +376,7 @@ extern "C" mxq_status moe_layout(
   hipStream_t s = as_stream(stream);
   int32_t* chunk_cnt = static_cast<int32_t*>(workspace);
   const int32_t cap = kind == MXQ_LAYOUT_MASKED ? capacity : 0;
-  const bool single = A <= kChunkMax;
+  const bool single = A <= kSingleMax;
   if (g.nc > 0 && !single) {
     layout_hist_kernel<<<g.nc, 256, (size_t)E * sizeof(int32_t), s>>>(
         topk_ids, A, expert_begin, E, g.chunk, chunk_cnt);

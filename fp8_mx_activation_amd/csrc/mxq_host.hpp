@@ -69,10 +69,15 @@ inline LayoutGeom layout_geom(int64_t A) {
   return g;
 }
 
-// Workspace: per-chunk expert counts [nc][E]; none when every assignment
-// fits one chunk (A <= kChunkMax), which the layout handles in one launch.
+// Up to this many assignments the layout runs as one launch in which every
+// block ranks the whole routing (at most four 64-assignment steps per
+// wavefront); above it the histogram + slots pair over chunks is faster.
+constexpr int64_t kSingleMax = 4096;
+
+// Workspace: per-chunk expert counts [nc][E]; none when the layout runs as
+// one launch (A <= kSingleMax).
 inline size_t layout_workspace_bytes(int64_t A, int32_t E) {
-  if (A <= kChunkMax) return 0;
+  if (A <= kSingleMax) return 0;
   LayoutGeom g = layout_geom(A);
   return (size_t)g.nc * (size_t)(E > 0 ? E : 0) * sizeof(int32_t);
 }

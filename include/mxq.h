@@ -97,7 +97,7 @@ int64_t moe_compact_row_bound(int64_t num_assignments,
 int32_t moe_should_use_masked(int32_t num_experts, int32_t num_local_experts);
 
 /* Workspace bytes moe_layout needs for T tokens, top-K, E local experts (0
- * when T*K <= 8192: one launch then handles the whole routing). */
+ * when T*K <= 4096: one launch then handles the whole routing). */
 size_t moe_layout_workspace_bytes(int64_t T, int32_t K, int32_t E);
 
 /* Workspace bytes requant_per_token_to_per_tensor needs. */

@@ -68,8 +68,8 @@ def test_host_helpers_match_oracle(mxq, ora):
 
 def test_workspace_sizes(mxq):
     assert mxq.moe_layout_workspace_bytes(0, 8, 256) == 0
-    assert mxq.moe_layout_workspace_bytes(1024, 8, 256) == 0   # one launch
-    assert mxq.moe_layout_workspace_bytes(1025, 8, 256) > 0
+    assert mxq.moe_layout_workspace_bytes(512, 8, 256) == 0    # one launch
+    assert mxq.moe_layout_workspace_bytes(513, 8, 256) > 0
     w = mxq.moe_layout_workspace_bytes(8192, 8, 256)
     assert 0 < w <= 64 * 256 * 4
     assert mxq.requant_workspace_bytes(16384, 4096) >= 4
@@ -222,7 +222,7 @@ def test_layout_validation(mxq):
     assert call(kind=5) == UNSUPPORTED
     assert call(kind=1, cap=0, rows=0) == INVALID
     assert call(kind=1, cap=16, rows=63) == INVALID  # E * cap = 64
-    # T*K above 8192 needs the per-chunk count workspace
+    # T*K above 4096 needs the per-chunk count workspace
     assert call(T=2048, K=8, ws=None) == WORKSPACE
     assert call(T=2048, K=8, wsb=4) == WORKSPACE
     assert call(ids=None) == INVALID

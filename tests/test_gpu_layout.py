@@ -111,14 +111,15 @@ def test_empty_batch(ora):
     assert (host(got["m_indices"]) == -1).all()
 
 
-@pytest.mark.parametrize("T,K,E", [(1024, 8, 1024), (1025, 8, 1024),
-                                   (683, 12, 300), (129, 8, 256),
-                                   (8192, 1, 7), (128, 8, 32)])
-def test_single_chunk_boundary(ora, T, K, E):
-    """Around T*K = 8192, where one launch (every block ranking the single
-    chunk) gives way to the histogram + slots pair: 8192 and 1032 take the
-    single path, 8200 and 8196 the two-launch path; masked capacity small
-    enough to overflow."""
+@pytest.mark.parametrize("T,K,E", [(512, 8, 1024), (513, 8, 1024),
+                                   (341, 12, 300), (342, 12, 300),
+                                   (129, 8, 256), (4096, 1, 7), (4097, 1, 7),
+                                   (128, 8, 32)])
+def test_single_launch_boundary(ora, T, K, E):
+    """Around T*K = 4096, where one launch (every block ranking the whole
+    routing) gives way to the histogram + slots pair: 4096, 4092, 1032 and
+    1024 take the single launch, 4104 and 4097 the pair; masked capacity
+    small enough to overflow."""
     rng = np.random.default_rng(T * K + E)
     ids = si.zipf_topk(rng, T, E, K) if E >= 2 * K else si.uniform_topk(
         rng, T, E, K)
