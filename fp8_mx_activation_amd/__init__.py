@@ -128,9 +128,33 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return t.data_ptr()
 
 
-def _dev(t: torch.Tensor, name: str) -> None:
+def _dev(t: torch.Tensor | None, name: str,
+         like: torch.Tensor | None = None) -> None:
+    """Every tensor handed to the library must live on the GPU (a host
+    pointer would fault the kernel), on the device of the call's inputs."""
+    if t is None:
+        return
     if not t.is_cuda:
         raise ValueError("%s must be a GPU tensor" % name)
+    if like is not None and t.device != like.device:
+        raise ValueError("%s is on %s, the inputs on %s"
+                         % (name, t.device, like.device))
+
+
+def _at_least(t: torch.Tensor, name: str, rows: int, cols: int) -> None:
+    """A 2-D buffer the kernels index up to [rows, cols)."""
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError("%s must be at least [%d, %d], got %s"
+                         % (name, rows, cols, tuple(t.shape)))
+
+
+def _src2dst(src2dst: torch.Tensor, like: torch.Tensor, T: int | None):
+    _dev(src2dst, "src2dst", like)
+    if src2dst.dtype != torch.int32 or src2dst.dim() != 2 or \
+            (T is not None and src2dst.shape[0] != T) or \
+            not src2dst.is_contiguous():
+        raise ValueError("src2dst must be contiguous int32 [T, K]")
+    return src2dst.shape[1]
 
 
 def _rows(t: torch.Tensor, name: str, dtypes) -> int:
@@ -219,10 +243,12 @@ def moe_layout(topk_ids: torch.Tensor, expert_begin: int,
         t = o.get(key)
         if t is None:
             t = torch.empty(shape, dtype=torch.int32, device=dev)
-        elif t.dtype != torch.int32 or tuple(t.shape) != tuple(shape) or \
-                not t.is_contiguous():
-            raise ValueError("out[%r] must be contiguous int32 %s"
-                             % (key, shape))
+        else:
+            _dev(t, "out[%r]" % key, ids)
+            if t.dtype != torch.int32 or tuple(t.shape) != tuple(shape) or \
+                    not t.is_contiguous():
+                raise ValueError("out[%r] must be contiguous int32 %s"
+                                 % (key, shape))
         return t
 
     counts = get("counts", (E,))
@@ -234,6 +260,10 @@ def moe_layout(topk_ids: torch.Tensor, expert_begin: int,
     need = moe_layout_workspace_bytes(T, K, E)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _dev(workspace, "workspace", ids)
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor")
     st = lib().moe_layout(_ptr(ids), T, K, expert_begin, E, k, block_e,
                           capacity, num_rows, _ptr(counts), _ptr(offsets),
                           _ptr(m_idx), _ptr(masked_m), _ptr(src2dst),
@@ -269,20 +299,19 @@ def moe_scatter_quant(x: torch.Tensor, src2dst: torch.Tensor, num_rows: int,
     code, G = SCALE_FORMATS[fmt]
     ld_x = _rows(x, "x", (torch.bfloat16,))
     T, H = x.shape
-    if src2dst.dtype != torch.int32 or src2dst.dim() != 2 or \
-            src2dst.shape[0] != T or not src2dst.is_contiguous():
-        raise ValueError("src2dst must be contiguous int32 [T, K]")
-    K = src2dst.shape[1]
+    K = _src2dst(src2dst, x, T)
     if q is None:
         q = _empty_rows_u8(num_rows, H, x.device)
     if scales is None:
         scales = torch.empty((num_rows, H // G), dtype=torch.uint8,
                              device=x.device)
+    _dev(q, "q", x)
+    _dev(scales, "scales", x)
     qq, ss = _u8(q), _u8(scales)
     ld_q = _rows(qq, "q", (torch.uint8,))
     ld_s = _rows(ss, "scales", (torch.uint8,))
-    if qq.shape[0] < num_rows or ss.shape[0] < num_rows:
-        raise ValueError("q/scales have fewer than num_rows rows")
+    _at_least(qq, "q", num_rows, H)
+    _at_least(ss, "scales", num_rows, H // G)
     st = lib().moe_scatter_quant(_ptr(x), ld_x, T, H, _ptr(src2dst), K, code,
                                  _ptr(qq), ld_q, _ptr(ss), ld_s, num_rows,
                                  _stream(x))
@@ -298,7 +327,7 @@ def mx_quant_live_rows(x: torch.Tensor, num_segments: int,
     ``num_segments`` equal segments (live rows at the head of each).
     Returns the padded ``(q, scales)``; only live rows are written."""
     _dev(x, "x")
-    _dev(live_counts, "live_counts")
+    _dev(live_counts, "live_counts", x)
     code, G = SCALE_FORMATS[fmt]
     ld_x = _rows(x, "x", (torch.bfloat16,))
     rows, H = x.shape
@@ -312,9 +341,13 @@ def mx_quant_live_rows(x: torch.Tensor, num_segments: int,
     if scales is None:
         scales = torch.empty((rows, H // G), dtype=torch.uint8,
                              device=x.device)
+    _dev(q, "q", x)
+    _dev(scales, "scales", x)
     qq, ss = _u8(q), _u8(scales)
     ld_q = _rows(qq, "q", (torch.uint8,))
     ld_s = _rows(ss, "scales", (torch.uint8,))
+    _at_least(qq, "q", rows, H)
+    _at_least(ss, "scales", rows, H // G)
     st = lib().mx_quant_live_rows(_ptr(x), ld_x, num_segments,
                                   rows // num_segments, _ptr(live_counts), H,
                                   code, _ptr(qq), ld_q, _ptr(ss), ld_s,
@@ -332,9 +365,12 @@ def packed_mn_scales(rows: int, groups: int, device) -> torch.Tensor:
 
 
 def _scale_place(scales: torch.Tensor | None, layout: str, rows: int,
-                 groups: int, device):
+                 groups: int, like: torch.Tensor):
     """(tensor, byte pointer tensor, row stride, quad stride) for a scale
-    placement; allocates the tensor when none is given."""
+    placement; allocates the tensor on ``like``'s device when none is
+    given."""
+    _dev(scales, "scales", like)
+    device = like.device
     if layout == "rows":
         if scales is None:
             scales = torch.empty((rows, groups), dtype=torch.uint8,
@@ -369,18 +405,15 @@ def moe_scatter_quant_ex(x: torch.Tensor, src2dst: torch.Tensor,
     code, G = SCALE_FORMATS[fmt]
     ld_x = _rows(x, "x", (torch.bfloat16,))
     T, H = x.shape
-    if src2dst.dtype != torch.int32 or src2dst.dim() != 2 or \
-            src2dst.shape[0] != T or not src2dst.is_contiguous():
-        raise ValueError("src2dst must be contiguous int32 [T, K]")
-    K = src2dst.shape[1]
+    K = _src2dst(src2dst, x, T)
     if q is None:
         q = _empty_rows_u8(num_rows, H, x.device)
+    _dev(q, "q", x)
     qq = _u8(q)
     ld_q = _rows(qq, "q", (torch.uint8,))
-    if qq.shape[0] < num_rows:
-        raise ValueError("q has fewer than num_rows rows")
+    _at_least(qq, "q", num_rows, H)
     scales, sp, rs, c4 = _scale_place(scales, scale_layout, num_rows, H // G,
-                                      x.device)
+                                      x)
     st = lib().moe_scatter_quant_ex(_ptr(x), ld_x, T, H, _ptr(src2dst), K,
                                     code, SCALE_RULES[rule], _ptr(qq), ld_q,
                                     _ptr(sp), rs, c4, num_rows, _stream(x))
@@ -396,7 +429,7 @@ def mx_quant_live_rows_ex(x: torch.Tensor, num_segments: int,
     """``mx_quant_live_rows`` with an exponent rule and scale layout as in
     ``moe_scatter_quant_ex``."""
     _dev(x, "x")
-    _dev(live_counts, "live_counts")
+    _dev(live_counts, "live_counts", x)
     code, G = SCALE_FORMATS[fmt]
     ld_x = _rows(x, "x", (torch.bfloat16,))
     rows, H = x.shape
@@ -407,10 +440,12 @@ def mx_quant_live_rows_ex(x: torch.Tensor, num_segments: int,
         raise ValueError("live_counts must be contiguous int32 [segments]")
     if q is None:
         q = _empty_rows_u8(rows, H, x.device)
+    _dev(q, "q", x)
     qq = _u8(q)
     ld_q = _rows(qq, "q", (torch.uint8,))
+    _at_least(qq, "q", rows, H)
     scales, sp, rs, c4 = _scale_place(scales, scale_layout, rows, H // G,
-                                      x.device)
+                                      x)
     st = lib().mx_quant_live_rows_ex(_ptr(x), ld_x, num_segments,
                                      rows // num_segments, _ptr(live_counts),
                                      H, code, SCALE_RULES[rule], _ptr(qq),
@@ -447,18 +482,28 @@ def requant_per_token_to_per_tensor(q_in: torch.Tensor,
     qi = _u8(q_in)
     ld_in = _rows(qi, "q_in", (torch.uint8,))
     T, H = qi.shape
+    _dev(token_scales, "token_scales", qi)
     if token_scales.dtype != torch.float32 or token_scales.numel() != T or \
             not token_scales.is_contiguous():
         raise ValueError("token_scales must be contiguous float32 [T]")
     if q_out is None:
         q_out = _empty_rows_u8(T, H, qi.device)
+    _dev(q_out, "q_out", qi)
     qo = _u8(q_out)
     ld_out = _rows(qo, "q_out", (torch.uint8,))
+    _at_least(qo, "q_out", T, H)
     if tensor_scale is None:
         tensor_scale = torch.empty(1, dtype=torch.float32, device=qi.device)
+    _dev(tensor_scale, "tensor_scale", qi)
+    if tensor_scale.dtype != torch.float32 or tensor_scale.numel() < 1:
+        raise ValueError("tensor_scale must be float32 with one element")
     need = requant_workspace_bytes(T, H)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=qi.device)
+    else:
+        _dev(workspace, "workspace", qi)
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor")
     st = lib().requant_per_token_to_per_tensor(
         _ptr(qi), ld_in, _ptr(token_scales), T, H, _ptr(qo), ld_out,
         tensor_scale.data_ptr(), _ptr(workspace), workspace.numel(),
@@ -476,18 +521,21 @@ def moe_combine(y: torch.Tensor, src2dst: torch.Tensor,
     _dev(y, "y")
     ld_y = _rows(y, "y", (torch.bfloat16,))
     num_rows, H = y.shape
-    if src2dst.dtype != torch.int32 or src2dst.dim() != 2 or \
-            not src2dst.is_contiguous():
-        raise ValueError("src2dst must be contiguous int32 [T, K]")
-    T, K = src2dst.shape
+    K = _src2dst(src2dst, y, None)
+    T = src2dst.shape[0]
+    _dev(topk_weights, "topk_weights", y)
     if topk_weights.dtype != torch.float32 or \
             tuple(topk_weights.shape) != (T, K) or \
             not topk_weights.is_contiguous():
         raise ValueError("topk_weights must be contiguous float32 [T, K]")
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=y.device)
+    _dev(out, "out", y)
+    if out.dtype not in OUT_DTYPES:
+        raise TypeError("out dtype must be one of %s" % list(OUT_DTYPES))
     code = OUT_DTYPES[out.dtype]
     ld_out = _rows(out, "out", (out.dtype,))
+    _at_least(out, "out", T, H)
     st = lib().moe_combine(_ptr(y), ld_y, num_rows, _ptr(src2dst),
                            _ptr(topk_weights), T, K, H, _ptr(out), ld_out,
                            code, _stream(y))
@@ -526,6 +574,11 @@ def moe_m_indices_from_psum(psum: torch.Tensor, num_rows: int,
     p = _psum(psum)
     if out is None:
         out = torch.empty(num_rows, dtype=torch.int32, device=p.device)
+    _dev(out, "out", p)
+    if out.dtype != torch.int32 or out.numel() < num_rows or \
+            not out.is_contiguous():
+        raise ValueError("out must be contiguous int32 with >= num_rows "
+                         "entries")
     st = lib().moe_m_indices_from_psum(_ptr(p), p.numel(), align, num_rows,
                                        _ptr(out), _stream(p))
     _check("moe_m_indices_from_psum", st)
@@ -544,6 +597,7 @@ def moe_expand_to_masked_slab(x: torch.Tensor, psum: torch.Tensor,
     Returns ``(slab, slab_scales, masked_m, flags)`` (device tensors)."""
     _dev(x, "x")
     p = _psum(psum)
+    _dev(p, "psum", x)
     E = p.numel()
     if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
         raise ValueError("x must be 2-D with unit column stride")
@@ -552,22 +606,40 @@ def moe_expand_to_masked_slab(x: torch.Tensor, psum: torch.Tensor,
     ld_x = (x.stride(0) if rows > 1 else cols) * esz
     if slab is None:
         slab = torch.empty((E * max_m, cols), dtype=x.dtype, device=x.device)
+    _dev(slab, "slab", x)
+    if slab.dim() != 2 or slab.element_size() != esz or \
+            (slab.shape[1] > 1 and slab.stride(1) != 1):
+        raise ValueError("slab must be 2-D, unit column stride, with x's "
+                         "element size")
+    _at_least(slab, "slab", E * max_m, cols)
     ld_slab = (slab.stride(0) if slab.shape[0] > 1 else cols) * esz
     masked_m = torch.empty(E, dtype=torch.int32, device=x.device)
     flags = torch.empty(1, dtype=torch.int32, device=x.device)
     xs_rs = xs_cs = ss_rs = ss_cs = s_cols = s_elem = 0
     if scales is not None:
-        _dev(scales, "scales")
+        _dev(scales, "scales", x)
         s_elem = scales.element_size()
+        if scales.dim() != 2:
+            raise ValueError("scales must be 2-D")
         if scales_col_major:
             s_cols = scales.shape[0]
+            if scales.shape[1] < rows:
+                raise ValueError("column-major scales need >= %d columns"
+                                 % rows)
             xs_rs, xs_cs = scales.stride(1) * s_elem, scales.stride(0) * s_elem
         else:
             s_cols = scales.shape[1]
+            if scales.shape[0] < rows:
+                raise ValueError("scales need >= %d rows" % rows)
             xs_rs, xs_cs = scales.stride(0) * s_elem, scales.stride(1) * s_elem
         if slab_scales is None:
             slab_scales = torch.empty((E * max_m, s_cols), dtype=scales.dtype,
                                       device=x.device)
+        _dev(slab_scales, "slab_scales", x)
+        if slab_scales.dim() != 2 or slab_scales.element_size() != s_elem:
+            raise ValueError("slab_scales must be 2-D with the scales' "
+                             "entry size")
+        _at_least(slab_scales, "slab_scales", E * max_m, s_cols)
         ss_rs = slab_scales.stride(0) * s_elem
         ss_cs = slab_scales.stride(1) * s_elem
     st = lib().moe_expand_to_masked_slab(
@@ -589,12 +661,24 @@ def moe_masked_slab_to_expand(slab: torch.Tensor, masked_m: torch.Tensor,
     (real rows only), multiplied by ``weights [rows]`` when given."""
     _dev(slab, "slab")
     p = _psum(psum)
+    _dev(p, "psum", slab)
+    E = p.numel()
+    _dev(masked_m, "masked_m", slab)
+    if masked_m.dtype != torch.int32 or masked_m.numel() < E or \
+            not masked_m.is_contiguous():
+        raise ValueError("masked_m must be contiguous int32 [E]")
     ld_slab = _rows(slab, "slab", (torch.bfloat16,))
     H = slab.shape[1]
+    _at_least(slab, "slab", E * max_m, H)
     if out is None:
+        if out_rows is None:
+            raise ValueError("give out or out_rows")
         out = torch.zeros((out_rows, H), dtype=torch.bfloat16,
                           device=slab.device)
+    _dev(out, "out", slab)
     ld_out = _rows(out, "out", (torch.bfloat16,))
+    _at_least(out, "out", 0, H)
+    _dev(weights, "weights", slab)
     if weights is not None and (weights.dtype != torch.float32 or
                                 not weights.is_contiguous() or
                                 weights.numel() < out.shape[0]):
@@ -641,12 +725,10 @@ def moe_scatter_rows(x: torch.Tensor, src2dst: torch.Tensor, num_rows: int,
     xx = _u8(x)
     ld_x = _rows(xx, "x", (torch.uint8,))
     T, rb = xx.shape
-    if src2dst.dtype != torch.int32 or src2dst.dim() != 2 or \
-            src2dst.shape[0] != T or not src2dst.is_contiguous():
-        raise ValueError("src2dst must be contiguous int32 [T, K]")
-    K = src2dst.shape[1]
+    K = _src2dst(src2dst, x, T)
     if out is None:
         out = _empty_rows_u8(num_rows, rb, x.device)
+    _dev(out, "out", x)
     oo = _u8(out)
     ld_o = _rows(oo, "out", (torch.uint8,))
     if oo.shape[0] < num_rows or oo.shape[1] < rb:
@@ -654,7 +736,7 @@ def moe_scatter_rows(x: torch.Tensor, src2dst: torch.Tensor, num_rows: int,
     xs_rs = xs_cs = os_rs = os_cs = 0
     cols, elem = 0, 1
     if scales is not None:
-        _dev(scales, "scales")
+        _dev(scales, "scales", x)
         elem = scales.element_size()
         xs_rs, xs_cs, cols = _scale_strides(scales, scales_col_major, T,
                                             "scales")
@@ -663,6 +745,7 @@ def moe_scatter_rows(x: torch.Tensor, src2dst: torch.Tensor, num_rows: int,
                 (num_rows, cols)
             out_scales = torch.empty(shape, dtype=scales.dtype,
                                      device=x.device)
+        _dev(out_scales, "out_scales", x)
         if out_scales.element_size() != elem:
             raise TypeError("out_scales must have the scales' entry size")
         os_rs, os_cs, ocols = _scale_strides(out_scales, out_scales_col_major,
@@ -688,7 +771,7 @@ def upscale_fp8_to_bf16(q: torch.Tensor, scales: torch.Tensor,
     ``scales_col_major``.  Rows of ``out`` at or past ``num_rows`` keep
     their contents."""
     _dev(q, "q")
-    _dev(scales, "scales")
+    _dev(scales, "scales", q)
     qq = _u8(q)
     ld_q = _rows(qq, "q", (torch.uint8,))
     rows, H = qq.shape
@@ -710,7 +793,9 @@ def upscale_fp8_to_bf16(q: torch.Tensor, scales: torch.Tensor,
         s_rs, s_cs = scales.stride(0), 1
     if out is None:
         out = torch.empty((rows, H), dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", q)
     ld_o = _rows(out, "out", (torch.bfloat16,))
+    _at_least(out, "out", n, H)
     st = lib().upscale_fp8_to_bf16(_ptr(qq), ld_q, _ptr(scales), s_rs, s_cs,
                                    n, H, group, _ptr(out), ld_o, _stream(q))
     _check("upscale_fp8_to_bf16", st)
@@ -727,7 +812,9 @@ def requant_weight_block_ue8m0(q: torch.Tensor, s_inv: torch.Tensor,
     scales [B, ceil(N/128), ceil(K/128)] -> (fp8 weights, UE8M0 scale bytes
     [B, nbn, nbk]).  ``inplace`` writes the weights over ``q``."""
     _dev(q, "q")
-    _dev(s_inv, "s_inv")
+    _dev(s_inv, "s_inv", q)
+    _dev(q_out, "q_out", q)
+    _dev(scales_out, "scales_out", q)
     qq = _u8(q)
     squeeze = qq.dim() == 2
     q3 = qq.unsqueeze(0) if squeeze else qq
