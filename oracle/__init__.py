@@ -272,6 +272,45 @@ def scatter_quant_ex(x_bf16, src2dst, G: int, num_rows: int, rule="ceil",
     return q, s
 
 
+def mfma_scales(scales_rows, H: int, G: int, tile_m: int, out=None,
+                fill=0):
+    """Reading R16: the scale placement read by gfx950's block-scaled MFMA
+    (v_mfma_scale_f32_32x32x64_f8f6f4 for tile_m = 32,
+    v_mfma_scale_f32_16x16x128_f8f6f4 for tile_m = 16) when the quantized
+    rows are its A operand.  No page fixes this layout; it follows the
+    instruction's operands (CDNA4 ISA, block-scaled matrix instructions):
+    instruction s of a row tile covers channels [s*KW, (s+1)*KW), KW =
+    64*32/tile_m; the scale of its block s*(64/tile_m) + l // tile_m of row
+    l % tile_m is read from lane l, byte s % 4 (op_sel) of the lane's 32-bit
+    scale register, one register per four instructions.  Stored as
+    [row tile, s // 4, lane, s % 4].
+
+    Built here from that instruction-side view: every (tile, word group,
+    lane, byte) is filled with the scale of the (row, block) the lane reads,
+    the group-G scale of block kb being scales_rows[row, kb*32 // G].
+    Positions past the last row or past H/32 blocks keep ``fill`` (or what
+    ``out`` holds).  Any dtype is accepted (the tests use labels)."""
+    S = np.asarray(scales_rows)
+    rows = S.shape[0]
+    nkb = H // 32
+    hh = 64 // tile_m                     # blocks per instruction
+    nkg = -(-nkb // (4 * hh))             # word groups per row tile
+    tiles = -(-rows // tile_m)
+    if out is None:
+        out = np.full((tiles, nkg, 64, 4), fill, S.dtype)
+    step = 256
+    for t0 in range(0, tiles, step):      # bounded index arrays
+        nt = min(step, tiles - t0)
+        mt, kg, lane, byte = np.indices((nt, nkg, 64, 4), dtype=np.int64)
+        mt += t0
+        instr = 4 * kg + byte
+        row = mt * tile_m + lane % tile_m
+        kb = instr * hh + lane // tile_m
+        ok = (row < rows) & (kb < nkb)
+        out[t0:t0 + nt][ok] = S[row[ok], (kb[ok] * 32) // G]
+    return out
+
+
 def unpack_mn_scales(packed: np.ndarray, rows: int, ng: int) -> np.ndarray:
     """[ceil(ng/4), ld_mn] uint32 words -> [rows, ng] scale bytes."""
     b = np.ascontiguousarray(packed).view(np.uint8).reshape(
