@@ -29,7 +29,7 @@ __all__ = [
     "requant_per_token_to_per_tensor", "moe_combine", "mxq_e4m3_encode_f32",
     "mxq_abi_version", "moe_m_indices_from_psum", "moe_expand_to_masked_slab",
     "moe_masked_slab_to_expand", "moe_scatter_rows", "upscale_fp8_to_bf16",
-    "requant_weight_block_ue8m0",
+    "requant_weight_block_ue8m0", "mxq_mfma_scale_bytes", "mfma_scales",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +40,7 @@ MXQ_ERR_CAPACITY_OVERFLOW = 3
 LAYOUT_KINDS = {"compact": 0, "masked": 1}
 SCALE_FORMATS = {"ue8m0_g128": (0, 128), "e8m0_g32": (1, 32)}
 SCALE_RULES = {"no_clip": 0, "ocp_floor": 1}
-SCALE_LAYOUTS = ("rows", "packed_mn")
+SCALE_LAYOUTS = ("rows", "packed_mn", "mfma32", "mfma16")
 OUT_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 
 _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, \
@@ -82,6 +82,11 @@ _SIGNATURES = {
     "requant_weight_block_ue8m0": (_i32, [_p, _i64, _i64, _p, _i64, _i64,
                                           _i32, _i32, _i32, _i32, _i32, _p,
                                           _p, _i64, _i64, _p]),
+    "mxq_mfma_scale_bytes": (_i64, [_i64, _i32, _i32]),
+    "moe_scatter_quant_mfma": (_i32, [_p, _i64, _i64, _i32, _p, _i32, _i32,
+                                      _i32, _p, _i64, _p, _i32, _i64, _p]),
+    "mx_quant_live_rows_mfma": (_i32, [_p, _i64, _i32, _i64, _p, _i32, _i32,
+                                       _i32, _p, _i64, _p, _i32, _p]),
     "mxq_status_string": (ctypes.c_char_p, [_i32]),
     "mxq_abi_version": (_i32, []),
 }
@@ -211,6 +216,14 @@ def requant_workspace_bytes(T: int, H: int) -> int:
 
 def mxq_abi_version() -> int:
     return int(lib().mxq_abi_version())
+
+
+def mxq_mfma_scale_bytes(rows: int, H: int, tile_m: int = 32) -> int:
+    """Bytes of the block-scaled MFMA scale placement (see mxq.h)."""
+    r = lib().mxq_mfma_scale_bytes(rows, H, tile_m)
+    if r < 0:
+        raise ValueError("invalid arguments to mxq_mfma_scale_bytes")
+    return int(r)
 
 
 # ------------------------------------------------------------------- layout
@@ -364,6 +377,31 @@ def packed_mn_scales(rows: int, groups: int, device) -> torch.Tensor:
                        dtype=torch.int32, device=device)
 
 
+def mfma_scales(rows: int, H: int, tile_m: int, device) -> torch.Tensor:
+    """Empty scale buffer in the block-scaled MFMA placement: uint8
+    ``[ceil(rows/tile_m), nkg, 64, 4]`` = (row tile, group of four
+    instructions, lane, op_sel byte); see ``mxq_mfma_scale_bytes``."""
+    n = mxq_mfma_scale_bytes(rows, H, tile_m)
+    tiles = -(-rows // tile_m)
+    nkg = n // (256 * tiles) if tiles else -(-(H // 32) // (4 * 64 // tile_m))
+    return torch.empty((tiles, nkg, 64, 4), dtype=torch.uint8, device=device)
+
+
+def _mfma_place(scales: torch.Tensor | None, layout: str, rows: int, H: int,
+                like: torch.Tensor):
+    """(tensor, tile_m) for an MFMA placement; allocates when none given."""
+    tm = int(layout[4:])
+    if scales is None:
+        return mfma_scales(rows, H, tm, like.device), tm
+    _dev(scales, "scales", like)
+    need = mxq_mfma_scale_bytes(rows, H, tm)
+    if scales.dtype != torch.uint8 or not scales.is_contiguous() or \
+            scales.numel() < need:
+        raise ValueError("MFMA-placed scales must be contiguous uint8 with "
+                         ">= %d bytes" % need)
+    return scales, tm
+
+
 def _scale_place(scales: torch.Tensor | None, layout: str, rows: int,
                  groups: int, like: torch.Tensor):
     """(tensor, byte pointer tensor, row stride, quad stride) for a scale
@@ -400,7 +438,9 @@ def moe_scatter_quant_ex(x: torch.Tensor, src2dst: torch.Tensor,
                          scales: torch.Tensor | None = None):
     """``moe_scatter_quant`` with an exponent ``rule`` (``"no_clip"`` or
     ``"ocp_floor"``) and a ``scale_layout``: ``"rows"`` (uint8 [rows,
-    groups]) or ``"packed_mn"`` (see ``packed_mn_scales``)."""
+    groups]), ``"packed_mn"`` (see ``packed_mn_scales``) or ``"mfma32"`` /
+    ``"mfma16"``, the block-scaled MFMA operand order (see
+    ``mfma_scales``)."""
     _dev(x, "x")
     code, G = SCALE_FORMATS[fmt]
     ld_x = _rows(x, "x", (torch.bfloat16,))
@@ -412,6 +452,13 @@ def moe_scatter_quant_ex(x: torch.Tensor, src2dst: torch.Tensor,
     qq = _u8(q)
     ld_q = _rows(qq, "q", (torch.uint8,))
     _at_least(qq, "q", num_rows, H)
+    if scale_layout in ("mfma32", "mfma16"):
+        scales, tm = _mfma_place(scales, scale_layout, num_rows, H, x)
+        st = lib().moe_scatter_quant_mfma(
+            _ptr(x), ld_x, T, H, _ptr(src2dst), K, code, SCALE_RULES[rule],
+            _ptr(qq), ld_q, _ptr(scales), tm, num_rows, _stream(x))
+        _check("moe_scatter_quant_mfma", st)
+        return q, scales
     scales, sp, rs, c4 = _scale_place(scales, scale_layout, num_rows, H // G,
                                       x)
     st = lib().moe_scatter_quant_ex(_ptr(x), ld_x, T, H, _ptr(src2dst), K,
@@ -444,6 +491,14 @@ def mx_quant_live_rows_ex(x: torch.Tensor, num_segments: int,
     qq = _u8(q)
     ld_q = _rows(qq, "q", (torch.uint8,))
     _at_least(qq, "q", rows, H)
+    if scale_layout in ("mfma32", "mfma16"):
+        scales, tm = _mfma_place(scales, scale_layout, rows, H, x)
+        st = lib().mx_quant_live_rows_mfma(
+            _ptr(x), ld_x, num_segments, rows // num_segments,
+            _ptr(live_counts), H, code, SCALE_RULES[rule], _ptr(qq), ld_q,
+            _ptr(scales), tm, _stream(x))
+        _check("mx_quant_live_rows_mfma", st)
+        return q, scales
     scales, sp, rs, c4 = _scale_place(scales, scale_layout, rows, H // G,
                                       x)
     st = lib().mx_quant_live_rows_ex(_ptr(x), ld_x, num_segments,

@@ -172,4 +172,22 @@ __device__ __forceinline__ int64_t scale_addr(int64_t row, int g, int64_t rs,
   return row * rs + (int64_t)(g >> 2) * c4 + (g & 3);
 }
 
+// Byte offset of the scale of 32-channel block kb of a row in the placement
+// that gfx950's block-scaled MFMA (v_mfma_scale_f32_{32x32x64,16x16x128}
+// _f8f6f4) reads, for tiles of tm = 2^tm_shift rows (32 or 16).  One
+// instruction spans 64/tm blocks of K; the scale of its block b of row r is
+// read from lane b * tm + r (whatever lanes hold the block's values), as one
+// byte of a 32-bit register, the byte (kb / (64/tm)) mod 4 selected by
+// op_sel, so one word per lane serves four consecutive instructions.  Words
+// are stored per (row tile, group of four instructions) as 64 lanes x 4
+// bytes; nkg is the number of such groups per row tile.
+__device__ __forceinline__ int64_t mfma_scale_addr(int64_t row, int kb,
+                                                   int tm_shift, int64_t nkg) {
+  const int hh_shift = 6 - tm_shift;  // log2 of blocks per instruction
+  const int lane = ((kb & ((1 << hh_shift) - 1)) << tm_shift) |
+                   (int)(row & ((1 << tm_shift) - 1));
+  const int64_t word_group = (row >> tm_shift) * nkg + (kb >> (hh_shift + 2));
+  return ((word_group << 6) + lane) * 4 + ((kb >> hh_shift) & 3);
+}
+
 }  // namespace mxq

@@ -17,6 +17,12 @@ namespace {
 
 using namespace mxq;
 
+// Scale placement of the quantizers: strided (row-major bytes or packed
+// MN-major words: s_rs, s_c4 as in scale_addr) or the block-scaled MFMA
+// operand order (s_rs = log2 of the tile rows, s_c4 = word groups per row
+// tile, as in mfma_scale_addr; each 32-channel block gets its own byte).
+enum Placement { kStrided = 0, kMfma = 1 };
+
 // One block per token, in two phases.  Phase 1: the block reads the token
 // row once (16-byte loads, a lane owns 16 channels), quantizes it and stages
 // the fp8 row and its scale bytes in LDS.  Phase 2: wavefront w writes
@@ -28,7 +34,7 @@ using namespace mxq;
 // merge in L2.  Destinations come from src2dst (uniform per block: scalar
 // loads); a token without a destination in [0, num_rows) is skipped before
 // its row is read.
-template <int G, int RULE>
+template <int G, int RULE, int PLACE>
 __global__ __launch_bounds__(1024) void scatter_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, int32_t H,
     const int32_t* __restrict__ src2dst, int32_t K, uint8_t* __restrict__ q,
@@ -63,14 +69,20 @@ __global__ __launch_bounds__(1024) void scatter_quant_kernel(
     uint8_t* qr = q + d * ld_q;
     for (int c = lane * 16; c < H; c += 64 * 16)
       store16_nt(qr + c, *reinterpret_cast<const u32x4*>(row + c));
-    for (int g = lane; g < ng; g += 64) s[scale_addr(d, g, s_rs, s_c4)] = row[H + g];
+    if constexpr (PLACE == kMfma) {
+      for (int kb = lane; kb < (H >> 5); kb += 64)
+        s[mfma_scale_addr(d, kb, (int)s_rs, s_c4)] = row[H + kb * 32 / G];
+    } else {
+      for (int g = lane; g < ng; g += 64)
+        s[scale_addr(d, g, s_rs, s_c4)] = row[H + g];
+    }
   }
 }
 
 // Send-side quant.  Segment g owns blocks [g*bps, (g+1)*bps); block i of a
 // segment handles its live rows i, i + bps, ...  The grid depends only on the
 // host arguments; blocks past the live count return at once.
-template <int G, int RULE>
+template <int G, int RULE, int PLACE>
 __global__ __launch_bounds__(1024) void live_rows_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, int64_t rps, int32_t bps,
     const int32_t* __restrict__ live, int32_t H, uint8_t* __restrict__ q,
@@ -89,7 +101,16 @@ __global__ __launch_bounds__(1024) void live_rows_kernel(
       int e;
       const u32x4 v = quant16<G, RULE>(a, b, e);
       store16(q + row * ld_q + col, v);
-      if (lead) s[scale_addr(row, col / G, s_rs, s_c4)] = (uint8_t)(e + 127);
+      if (lead) {
+        const uint8_t sb = (uint8_t)(e + 127);
+        if constexpr (PLACE == kMfma) {
+#pragma unroll
+          for (int u = 0; u < G / 32; ++u)
+            s[mfma_scale_addr(row, col / 32 + u, (int)s_rs, s_c4)] = sb;
+        } else {
+          s[scale_addr(row, col / G, s_rs, s_c4)] = sb;
+        }
+      }
     }
   }
 }
@@ -128,40 +149,89 @@ bool scale_place_ok(int64_t rs, int64_t c4, int64_t groups, int64_t rows) {
   return false;
 }
 
-template <int G>
+template <int G, int PLACE>
 void launch_scatter(int rule, unsigned T, int threads, size_t lds,
                     hipStream_t s, const uint16_t* x, int64_t ld_x, int32_t H,
                     const int32_t* src2dst, int32_t K, uint8_t* q,
                     int64_t ld_q, uint8_t* sc, int64_t rs, int64_t c4,
                     int64_t num_rows) {
   if (rule == MXQ_RULE_OCP_FLOOR)
-    scatter_quant_kernel<G, kOcpFloor><<<T, threads, lds, s>>>(
+    scatter_quant_kernel<G, kOcpFloor, PLACE><<<T, threads, lds, s>>>(
         x, ld_x, H, src2dst, K, q, ld_q, sc, rs, c4, num_rows);
   else
-    scatter_quant_kernel<G, kNoClip><<<T, threads, lds, s>>>(
+    scatter_quant_kernel<G, kNoClip, PLACE><<<T, threads, lds, s>>>(
         x, ld_x, H, src2dst, K, q, ld_q, sc, rs, c4, num_rows);
 }
 
-template <int G>
+template <int G, int PLACE>
 void launch_live(int rule, unsigned blocks, int threads, hipStream_t s,
                  const uint16_t* x, int64_t ld_x, int64_t rps, int32_t bps,
                  const int32_t* live, int32_t H, uint8_t* q, int64_t ld_q,
                  uint8_t* sc, int64_t rs, int64_t c4) {
   if (rule == MXQ_RULE_OCP_FLOOR)
-    live_rows_kernel<G, kOcpFloor><<<blocks, threads, 0, s>>>(
+    live_rows_kernel<G, kOcpFloor, PLACE><<<blocks, threads, 0, s>>>(
         x, ld_x, rps, bps, live, H, q, ld_q, sc, rs, c4);
   else
-    live_rows_kernel<G, kNoClip><<<blocks, threads, 0, s>>>(
+    live_rows_kernel<G, kNoClip, PLACE><<<blocks, threads, 0, s>>>(
         x, ld_x, rps, bps, live, H, q, ld_q, sc, rs, c4);
 }
 
-}  // namespace
+// Word groups per row tile of the MFMA placement: one group holds the scales
+// of four instructions, each spanning 64/tm blocks of 32 channels.
+int64_t mfma_word_groups(int32_t H, int32_t tile_m) {
+  return ceil_div(H / 32, 4 * (64 / tile_m));
+}
 
-extern "C" mxq_status moe_scatter_quant_ex(
-    const void* x_bf16, int64_t ld_x, int64_t T, int32_t H,
-    const int32_t* src2dst, int32_t K, mxq_scale_fmt fmt, mxq_scale_rule rule,
-    void* q_fp8, int64_t ld_q, void* scales, int64_t scale_row_stride,
-    int64_t scale_quad_stride, int64_t num_rows, void* stream) {
+int mfma_tile_shift(int32_t tile_m) {
+  return tile_m == 32 ? 5 : (tile_m == 16 ? 4 : -1);
+}
+
+// Shared body of the scatter entry points; `place` selects the scale
+// placement, whose own arguments (rs, c4) the caller has checked.
+mxq_status scatter_quant_impl(const void* x_bf16, int64_t ld_x, int64_t T,
+                              int32_t H, const int32_t* src2dst, int32_t K,
+                              mxq_scale_fmt fmt, mxq_scale_rule rule,
+                              void* q_fp8, int64_t ld_q, void* scales,
+                              int place, int64_t rs, int64_t c4,
+                              int64_t num_rows, void* stream) {
+  const int G = group_of(fmt);
+  if (T == 0 || K == 0 || num_rows == 0) return MXQ_OK;
+
+  // 1024 threads: at most two tokens in flight per CU, which keeps the
+  // number of concurrent destination-row write streams low.
+  const int threads = 1024;
+  const size_t lds = (size_t)H + (size_t)(H / G);
+  hipStream_t s = as_stream(stream);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* q = static_cast<uint8_t*>(q_fp8);
+  uint8_t* sc = static_cast<uint8_t*>(scales);
+  if (place == kMfma) {
+    if (G == 128)
+      launch_scatter<128, kMfma>(rule, (unsigned)T, threads, lds, s, x, ld_x,
+                                 H, src2dst, K, q, ld_q, sc, rs, c4, num_rows);
+    else
+      launch_scatter<32, kMfma>(rule, (unsigned)T, threads, lds, s, x, ld_x,
+                                H, src2dst, K, q, ld_q, sc, rs, c4, num_rows);
+  } else {
+    if (G == 128)
+      launch_scatter<128, kStrided>(rule, (unsigned)T, threads, lds, s, x,
+                                    ld_x, H, src2dst, K, q, ld_q, sc, rs, c4,
+                                    num_rows);
+    else
+      launch_scatter<32, kStrided>(rule, (unsigned)T, threads, lds, s, x,
+                                   ld_x, H, src2dst, K, q, ld_q, sc, rs, c4,
+                                   num_rows);
+  }
+  return launch_status();
+}
+
+// Checks shared by the scatter entry points (everything but the scale
+// placement).  Returns MXQ_OK when the call may go on.
+mxq_status scatter_args_ok(const void* x_bf16, int64_t ld_x, int64_t T,
+                           int32_t H, const int32_t* src2dst, int32_t K,
+                           mxq_scale_fmt fmt, mxq_scale_rule rule,
+                           const void* q_fp8, int64_t ld_q,
+                           const void* scales, int64_t num_rows) {
   const int G = group_of(fmt);
   if (G == 0 || (rule != MXQ_RULE_NO_CLIP && rule != MXQ_RULE_OCP_FLOOR))
     return MXQ_ERR_UNSUPPORTED;
@@ -174,30 +244,99 @@ extern "C" mxq_status moe_scatter_quant_ex(
     return MXQ_ERR_INVALID_ARGUMENT;
   if (num_rows > 0 && (q_fp8 == nullptr || scales == nullptr))
     return MXQ_ERR_INVALID_ARGUMENT;
-  if (ld_q < H ||
-      !scale_place_ok(scale_row_stride, scale_quad_stride, H / G, num_rows))
-    return MXQ_ERR_INVALID_ARGUMENT;
+  if (ld_q < H) return MXQ_ERR_INVALID_ARGUMENT;
   if (!rows_ok_bf16(x_bf16, ld_x) || (num_rows > 0 && !rows_ok_u8(q_fp8, ld_q)))
     return MXQ_ERR_INVALID_ARGUMENT;
-  if (num_rows == 0) return MXQ_OK;
+  return MXQ_OK;
+}
 
-  // 1024 threads: at most two tokens in flight per CU, which keeps the
-  // number of concurrent destination-row write streams low.
-  const int threads = 1024;
-  const size_t lds = (size_t)H + (size_t)(H / G);
+// Shared body of the live-row entry points, as scatter_quant_impl.
+mxq_status live_rows_impl(const void* x_bf16, int64_t ld_x,
+                          int32_t num_segments, int64_t rows_per_segment,
+                          const int32_t* live_counts, int32_t H,
+                          mxq_scale_fmt fmt, mxq_scale_rule rule, void* q_fp8,
+                          int64_t ld_q, void* scales, int place, int64_t rs,
+                          int64_t c4, void* stream) {
+  const int G = group_of(fmt);
+  // About 1024 blocks in all, at most one per padded row of a segment.
+  int64_t bps = ceil_div(1024, num_segments);
+  if (bps > rows_per_segment) bps = rows_per_segment;
+  if (bps < 1) bps = 1;
+  const int64_t blocks = bps * num_segments;
+  if (blocks > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
+  const int threads = row_block_threads(H, 16);
   hipStream_t s = as_stream(stream);
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   uint8_t* q = static_cast<uint8_t*>(q_fp8);
   uint8_t* sc = static_cast<uint8_t*>(scales);
-  if (G == 128)
-    launch_scatter<128>(rule, (unsigned)T, threads, lds, s, x, ld_x, H,
-                        src2dst, K, q, ld_q, sc, scale_row_stride,
-                        scale_quad_stride, num_rows);
-  else
-    launch_scatter<32>(rule, (unsigned)T, threads, lds, s, x, ld_x, H,
-                       src2dst, K, q, ld_q, sc, scale_row_stride,
-                       scale_quad_stride, num_rows);
+  const int32_t b32 = (int32_t)bps;
+  if (place == kMfma) {
+    if (G == 32)
+      launch_live<32, kMfma>(rule, (unsigned)blocks, threads, s, x, ld_x,
+                             rows_per_segment, b32, live_counts, H, q, ld_q,
+                             sc, rs, c4);
+    else
+      launch_live<128, kMfma>(rule, (unsigned)blocks, threads, s, x, ld_x,
+                              rows_per_segment, b32, live_counts, H, q, ld_q,
+                              sc, rs, c4);
+  } else {
+    if (G == 32)
+      launch_live<32, kStrided>(rule, (unsigned)blocks, threads, s, x, ld_x,
+                                rows_per_segment, b32, live_counts, H, q,
+                                ld_q, sc, rs, c4);
+    else
+      launch_live<128, kStrided>(rule, (unsigned)blocks, threads, s, x, ld_x,
+                                 rows_per_segment, b32, live_counts, H, q,
+                                 ld_q, sc, rs, c4);
+  }
   return launch_status();
+}
+
+// Checks shared by the live-row entry points except the scale placement.
+// Sets *rows to the padded row count.  Returns MXQ_OK when the call may go
+// on and there is work (*rows > 0), or an error, or MXQ_OK with *rows = 0.
+mxq_status live_args_ok(const void* x_bf16, int64_t ld_x,
+                        int32_t num_segments, int64_t rows_per_segment,
+                        const int32_t* live_counts, int32_t H,
+                        mxq_scale_fmt fmt, mxq_scale_rule rule,
+                        const void* q_fp8, int64_t ld_q, const void* scales,
+                        int64_t* rows) {
+  *rows = 0;
+  const int G = group_of(fmt);
+  if (G == 0 || (rule != MXQ_RULE_NO_CLIP && rule != MXQ_RULE_OCP_FLOOR))
+    return MXQ_ERR_UNSUPPORTED;
+  if (num_segments < 0 || rows_per_segment < 0 || H <= 0 || H % G != 0)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (num_segments == 0 || rows_per_segment == 0) return MXQ_OK;
+  const int64_t n = (int64_t)num_segments * rows_per_segment;
+  if (n > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
+  if (x_bf16 == nullptr || live_counts == nullptr || q_fp8 == nullptr ||
+      scales == nullptr)
+    return MXQ_ERR_INVALID_ARGUMENT;
+  if (ld_x < H || ld_q < H) return MXQ_ERR_INVALID_ARGUMENT;
+  if (!rows_ok_bf16(x_bf16, ld_x) || !rows_ok_u8(q_fp8, ld_q))
+    return MXQ_ERR_INVALID_ARGUMENT;
+  *rows = n;
+  return MXQ_OK;
+}
+
+}  // namespace
+
+extern "C" mxq_status moe_scatter_quant_ex(
+    const void* x_bf16, int64_t ld_x, int64_t T, int32_t H,
+    const int32_t* src2dst, int32_t K, mxq_scale_fmt fmt, mxq_scale_rule rule,
+    void* q_fp8, int64_t ld_q, void* scales, int64_t scale_row_stride,
+    int64_t scale_quad_stride, int64_t num_rows, void* stream) {
+  const mxq_status st = scatter_args_ok(x_bf16, ld_x, T, H, src2dst, K, fmt,
+                                        rule, q_fp8, ld_q, scales, num_rows);
+  if (st != MXQ_OK) return st;
+  if (T == 0 || K == 0) return MXQ_OK;
+  if (!scale_place_ok(scale_row_stride, scale_quad_stride,
+                      H / group_of(fmt), num_rows))
+    return MXQ_ERR_INVALID_ARGUMENT;
+  return scatter_quant_impl(x_bf16, ld_x, T, H, src2dst, K, fmt, rule, q_fp8,
+                            ld_q, scales, kStrided, scale_row_stride,
+                            scale_quad_stride, num_rows, stream);
 }
 
 extern "C" mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x,
@@ -212,49 +351,45 @@ extern "C" mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x,
                               num_rows, stream);
 }
 
+extern "C" int64_t mxq_mfma_scale_bytes(int64_t rows, int32_t H,
+                                        int32_t tile_m) {
+  if (rows < 0 || H <= 0 || H % 32 != 0 || mfma_tile_shift(tile_m) < 0)
+    return -1;
+  return ceil_div(rows, tile_m) * mfma_word_groups(H, tile_m) * 256;
+}
+
+extern "C" mxq_status moe_scatter_quant_mfma(
+    const void* x_bf16, int64_t ld_x, int64_t T, int32_t H,
+    const int32_t* src2dst, int32_t K, mxq_scale_fmt fmt, mxq_scale_rule rule,
+    void* q_fp8, int64_t ld_q, void* scales, int32_t tile_m, int64_t num_rows,
+    void* stream) {
+  const mxq_status st = scatter_args_ok(x_bf16, ld_x, T, H, src2dst, K, fmt,
+                                        rule, q_fp8, ld_q, scales, num_rows);
+  if (st != MXQ_OK) return st;
+  const int shift = mfma_tile_shift(tile_m);
+  if (shift < 0) return MXQ_ERR_INVALID_ARGUMENT;
+  return scatter_quant_impl(x_bf16, ld_x, T, H, src2dst, K, fmt, rule, q_fp8,
+                            ld_q, scales, kMfma, shift,
+                            mfma_word_groups(H, tile_m), num_rows, stream);
+}
+
 extern "C" mxq_status mx_quant_live_rows_ex(
     const void* x_bf16, int64_t ld_x, int32_t num_segments,
     int64_t rows_per_segment, const int32_t* live_counts, int32_t H,
     mxq_scale_fmt fmt, mxq_scale_rule rule, void* q_fp8, int64_t ld_q,
     void* scales, int64_t scale_row_stride, int64_t scale_quad_stride,
     void* stream) {
-  const int G = group_of(fmt);
-  if (G == 0 || (rule != MXQ_RULE_NO_CLIP && rule != MXQ_RULE_OCP_FLOOR))
-    return MXQ_ERR_UNSUPPORTED;
-  if (num_segments < 0 || rows_per_segment < 0 || H <= 0 || H % G != 0)
+  int64_t rows = 0;
+  const mxq_status st =
+      live_args_ok(x_bf16, ld_x, num_segments, rows_per_segment, live_counts,
+                   H, fmt, rule, q_fp8, ld_q, scales, &rows);
+  if (st != MXQ_OK || rows == 0) return st;
+  if (!scale_place_ok(scale_row_stride, scale_quad_stride,
+                      H / group_of(fmt), rows))
     return MXQ_ERR_INVALID_ARGUMENT;
-  if (num_segments == 0 || rows_per_segment == 0) return MXQ_OK;
-  const int64_t rows = (int64_t)num_segments * rows_per_segment;
-  if (rows > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
-  if (x_bf16 == nullptr || live_counts == nullptr || q_fp8 == nullptr ||
-      scales == nullptr)
-    return MXQ_ERR_INVALID_ARGUMENT;
-  if (ld_x < H || ld_q < H ||
-      !scale_place_ok(scale_row_stride, scale_quad_stride, H / G, rows))
-    return MXQ_ERR_INVALID_ARGUMENT;
-  if (!rows_ok_bf16(x_bf16, ld_x) || !rows_ok_u8(q_fp8, ld_q))
-    return MXQ_ERR_INVALID_ARGUMENT;
-
-  // About 1024 blocks in all, at most one per padded row of a segment.
-  int64_t bps = ceil_div(1024, num_segments);
-  if (bps > rows_per_segment) bps = rows_per_segment;
-  if (bps < 1) bps = 1;
-  const int64_t blocks = bps * num_segments;
-  if (blocks > INT32_MAX) return MXQ_ERR_INVALID_ARGUMENT;
-  const int threads = row_block_threads(H, 16);
-  hipStream_t s = as_stream(stream);
-  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
-  uint8_t* q = static_cast<uint8_t*>(q_fp8);
-  uint8_t* sc = static_cast<uint8_t*>(scales);
-  if (G == 32)
-    launch_live<32>(rule, (unsigned)blocks, threads, s, x, ld_x,
-                    rows_per_segment, (int32_t)bps, live_counts, H, q, ld_q,
-                    sc, scale_row_stride, scale_quad_stride);
-  else
-    launch_live<128>(rule, (unsigned)blocks, threads, s, x, ld_x,
-                     rows_per_segment, (int32_t)bps, live_counts, H, q, ld_q,
-                     sc, scale_row_stride, scale_quad_stride);
-  return launch_status();
+  return live_rows_impl(x_bf16, ld_x, num_segments, rows_per_segment,
+                        live_counts, H, fmt, rule, q_fp8, ld_q, scales,
+                        kStrided, scale_row_stride, scale_quad_stride, stream);
 }
 
 extern "C" mxq_status mx_quant_live_rows(const void* x_bf16, int64_t ld_x,
@@ -267,6 +402,24 @@ extern "C" mxq_status mx_quant_live_rows(const void* x_bf16, int64_t ld_x,
   return mx_quant_live_rows_ex(x_bf16, ld_x, num_segments, rows_per_segment,
                                live_counts, H, fmt, MXQ_RULE_NO_CLIP, q_fp8,
                                ld_q, scales, ld_s, 4, stream);
+}
+
+extern "C" mxq_status mx_quant_live_rows_mfma(
+    const void* x_bf16, int64_t ld_x, int32_t num_segments,
+    int64_t rows_per_segment, const int32_t* live_counts, int32_t H,
+    mxq_scale_fmt fmt, mxq_scale_rule rule, void* q_fp8, int64_t ld_q,
+    void* scales, int32_t tile_m, void* stream) {
+  int64_t rows = 0;
+  const mxq_status st =
+      live_args_ok(x_bf16, ld_x, num_segments, rows_per_segment, live_counts,
+                   H, fmt, rule, q_fp8, ld_q, scales, &rows);
+  if (st != MXQ_OK) return st;
+  const int shift = mfma_tile_shift(tile_m);
+  if (shift < 0) return MXQ_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return MXQ_OK;
+  return live_rows_impl(x_bf16, ld_x, num_segments, rows_per_segment,
+                        live_counts, H, fmt, rule, q_fp8, ld_q, scales, kMfma,
+                        shift, mfma_word_groups(H, tile_m), stream);
 }
 
 extern "C" mxq_status mxq_e4m3_encode_f32(const float* in, int64_t n,

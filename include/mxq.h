@@ -194,6 +194,40 @@ mxq_status moe_scatter_quant_ex(const void* x_bf16, int64_t ld_x, int64_t T,
                                 int64_t scale_quad_stride, int64_t num_rows,
                                 void* stream);
 
+/* Scale placement read directly by gfx950's block-scaled MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4 with tile_m = 32, or
+ * v_mfma_scale_f32_16x16x128_f8f6f4 with tile_m = 16) when the quantized
+ * rows are its A (or B) operand [P3 Review highlights item 3 and P4 impl.
+ * item 1: scales are stored the way the consuming GEMM reads them].  One
+ * instruction covers a tile of tile_m rows by 64*32/tile_m channels; the
+ * scale of its 32-channel block h (h < 64/tile_m) of row r is read from lane
+ * l = h*tile_m + r as one byte of a 32-bit register, selected by op_sel, so
+ * one register serves four consecutive instructions.  Byte
+ * offset of the scale of 32-channel block kb of row d:
+ *     ((d / tile_m) * nkg + kb / (4 * 64/tile_m)) * 256
+ *   + ((kb % (64/tile_m)) * tile_m + d % tile_m) * 4
+ *   + (kb / (64/tile_m)) % 4,
+ * nkg = ceil((H/32) / (4 * 64/tile_m)): per row tile, nkg runs of 64 words,
+ * one word per lane.  With group 128 each scale byte is written to its four
+ * 32-channel blocks (the instruction's block is 32 channels).  Bytes of rows
+ * past the last row and of blocks past H/32 are never written.
+ *
+ * Size of that placement for `rows` rows (rounded up to whole tiles) of H
+ * channels: ceil(rows / tile_m) * nkg * 256 bytes.  Returns -1 unless
+ * rows >= 0, H > 0, H % 32 == 0 and tile_m is 16 or 32.  Pure host function. */
+int64_t mxq_mfma_scale_bytes(int64_t rows, int32_t H, int32_t tile_m);
+
+/* moe_scatter_quant_ex with the scales in the block-scaled MFMA placement
+ * above: `scales` holds mxq_mfma_scale_bytes(num_rows, H, tile_m) bytes.
+ * Errors as moe_scatter_quant_ex; tile_m other than 16 or 32 is
+ * MXQ_ERR_INVALID_ARGUMENT. */
+mxq_status moe_scatter_quant_mfma(const void* x_bf16, int64_t ld_x, int64_t T,
+                                  int32_t H, const int32_t* src2dst,
+                                  int32_t K, mxq_scale_fmt fmt,
+                                  mxq_scale_rule rule, void* q_fp8,
+                                  int64_t ld_q, void* scales, int32_t tile_m,
+                                  int64_t num_rows, void* stream);
+
 /* Send-side quant over live rows only [P4 Features & motivation and impl.
  * item 1: quantize on the sender over the live tokens, not the padded
  * receive buffer; 224 one-byte scales per 7168-wide row].
@@ -221,6 +255,18 @@ mxq_status mx_quant_live_rows_ex(const void* x_bf16, int64_t ld_x,
                                  void* q_fp8, int64_t ld_q, void* scales,
                                  int64_t scale_row_stride,
                                  int64_t scale_quad_stride, void* stream);
+
+/* mx_quant_live_rows_ex with the scales in the block-scaled MFMA placement
+ * (see mxq_mfma_scale_bytes): `scales` holds
+ * mxq_mfma_scale_bytes(num_segments * rows_per_segment, H, tile_m) bytes and
+ * only the bytes of live rows are written. */
+mxq_status mx_quant_live_rows_mfma(const void* x_bf16, int64_t ld_x,
+                                   int32_t num_segments,
+                                   int64_t rows_per_segment,
+                                   const int32_t* live_counts, int32_t H,
+                                   mxq_scale_fmt fmt, mxq_scale_rule rule,
+                                   void* q_fp8, int64_t ld_q, void* scales,
+                                   int32_t tile_m, void* stream);
 
 /* ------------------------------------------------------------- requant */
 

@@ -141,6 +141,46 @@ def test_scatter_quant_ex_validation(mxq):
     assert call(rows=0, q=None, s=None, rs=4, c4=0) == 0
 
 
+def test_mfma_placement_validation(mxq):
+    """The block-scaled MFMA placement: size query and entry-point checks
+    (every rejected call returns before anything is enqueued)."""
+    L = mxq.lib()
+    assert L.mxq_mfma_scale_bytes(98048, 7168, 32) == 98048 * 224
+    assert L.mxq_mfma_scale_bytes(98048, 7168, 16) == 98048 * 224
+    assert L.mxq_mfma_scale_bytes(33, 7200, 32) == 2 * 29 * 256
+    assert L.mxq_mfma_scale_bytes(0, 7168, 32) == 0
+    for bad in [(-1, 7168, 32), (4, 0, 32), (4, 7169, 32), (4, 7168, 8),
+                (4, 7168, 64), (4, 96 + 16, 16)]:
+        assert L.mxq_mfma_scale_bytes(*bad) == -1, bad
+    ok = dict(x=FAKE, ld_x=640, T=4, H=640, s2d=FAKE, K=2, fmt=1, rule=0,
+              q=FAKE, ld_q=640, s=FAKE, tm=32, rows=18)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.moe_scatter_quant_mfma(a["x"], a["ld_x"], a["T"], a["H"],
+                                        a["s2d"], a["K"], a["fmt"], a["rule"],
+                                        a["q"], a["ld_q"], a["s"], a["tm"],
+                                        a["rows"], None)
+
+    def live(**kw):
+        a = dict(ok, **kw)
+        return L.mx_quant_live_rows_mfma(a["x"], a["ld_x"], 3, 6, FAKE, a["H"],
+                                         a["fmt"], a["rule"], a["q"],
+                                         a["ld_q"], a["s"], a["tm"], None)
+
+    for f in (call, live):
+        assert f(tm=8) == INVALID
+        assert f(tm=64) == INVALID
+        assert f(rule=2) == UNSUPPORTED
+        assert f(fmt=7) == UNSUPPORTED
+        assert f(s=None) == INVALID
+        assert f(ld_q=639) == INVALID
+        assert f(H=650) == INVALID            # not a whole number of groups
+    assert call(T=0) == 0
+    assert call(rows=0, q=None, s=None) == 0
+    assert live(H=640, x=None) == INVALID
+
+
 def test_upscale_and_weight_requant_validation(mxq):
     L = mxq.lib()
 

@@ -22,12 +22,15 @@ def labels(rows, ng):
                                     (33, 7200), (100, 96), (64, 4096)])
 def test_every_block_once(tm, rows, H):
     """Each (row, block) lands on exactly one byte; nothing else is
-    written."""
+    written; the size matches the library's host query."""
     nkb = H // 32
     out = oracle.mfma_scales(labels(rows, nkb), H, 32, tm, fill=-1)
     got = out[out >= 0]
     assert got.size == rows * nkb
     assert np.array_equal(np.sort(got), np.arange(rows * nkb))
+    import fp8_mx_activation_amd as mxq
+    if __import__("os").path.exists(mxq.LIB_PATH):
+        assert out.size == mxq.mxq_mfma_scale_bytes(rows, H, tm)
 
 
 def byte_at(out, offset):
