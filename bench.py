@@ -347,7 +347,7 @@ def main():
     variants = srows = None
     if not args.no_rows:
         variants = scale_variant_rows(torch, mxq, x, lay_out["src2dst"], R,
-                                      H, q, B_sq, dev)
+                                      H, q, B_sq, A, dev)
         srows = scatter_rows_row(torch, mxq, x, lay_out["src2dst"], R, H, q,
                                  T, K, A, dev)
     del q, s, out
@@ -432,7 +432,7 @@ def layout_sweep(torch, mxq, si, dev, H=7168, K=8):
 
 # ------------------------------------------------- separately timed rows
 
-def scale_variant_rows(torch, mxq, x, src2dst, R, H, q, B_sq, dev):
+def scale_variant_rows(torch, mxq, x, src2dst, R, H, q, B_sq, A, dev):
     """The prefill scatter under each exponent rule and scale placement,
     timed back to back (the plain entry point beside them, timed the same
     way)."""
@@ -452,6 +452,16 @@ def scale_variant_rows(torch, mxq, x, src2dst, R, H, q, B_sq, dev):
             out["%s/%s_us" % (rule, layout)] = round(us, 2)
             out["%s/%s_gbs" % (rule, layout)] = round(
                 B_sq / (us * 1e-6) / 1e9, 2)
+    # the block-scaled MFMA placement: one byte per 32-channel block, so
+    # each group-128 scale is written four times (224 bytes per row)
+    B_mfma = B_sq + A * (H // 32 - H // 128)
+    out["mfma_algorithmic_bytes"] = B_mfma
+    for layout in ("mfma32", "mfma16"):
+        sc = mxq.mfma_scales(R, H, int(layout[4:]), dev)
+        us = time_calls(torch, lambda: mxq.moe_scatter_quant_ex(
+            x, src2dst, R, "ue8m0_g128", "no_clip", layout, q=q, scales=sc))
+        out["no_clip/%s_us" % layout] = round(us, 2)
+        out["no_clip/%s_gbs" % layout] = round(B_mfma / (us * 1e-6) / 1e9, 2)
     return out
 
 
@@ -521,6 +531,13 @@ def other_rows(torch, mxq, si, dev):
         xs, 8, lc, q=qs, scales=ss), reps=5)
     res["padded_grid_us"] = round(us_pad, 2)
     res["padded_over_live_14x8"] = round(us_pad / res["14x8"]["us"], 1)
+    # the same 14x8 live rows with the scales in the block-scaled MFMA
+    # placement (32-row tiles)
+    lc = torch.tensor([14] * 8, dtype=torch.int32, device=dev)
+    sm = mxq.mfma_scales(24576, 7168, 32, dev)
+    us = time_calls(torch, lambda: mxq.mx_quant_live_rows_ex(
+        xs, 8, lc, "e8m0_g32", scale_layout="mfma32", q=qs, scales=sm))
+    res["14x8_mfma32_us"] = round(us, 2)
     res["workload"] = ("24576 x 7168 bf16 padded buffer = 8 segments of "
                        "3072 rows, e8m0 group-32 (224 scales/row)")
     rows["live_rows_mx"] = res
