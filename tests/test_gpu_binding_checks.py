@@ -15,7 +15,7 @@ T, K, H, R = 4, 2, 256, 8
 # entry points that launch nothing; every other one is replaced below
 HOST_ONLY = {"moe_compact_row_bound", "moe_should_use_masked",
              "moe_layout_workspace_bytes", "requant_workspace_bytes",
-             "mxq_status_string", "mxq_abi_version"}
+             "mxq_status_string", "mxq_abi_version", "mxq_mfma_scale_bytes"}
 
 
 class NoLaunch:
@@ -73,6 +73,8 @@ def host_argument_calls(g):
         "scatter_ex packed scales": lambda: mxq.moe_scatter_quant_ex(
             x, ids, R, scale_layout="packed_mn",
             scales=h(1, R, dtype=torch.int32)),  # packed [ceil(2/4), 8]
+        "scatter_ex mfma scales": lambda: mxq.moe_scatter_quant_ex(
+            x, ids, R, scale_layout="mfma32", scales=h(1, 1, 64, 4)),
         "live counts": lambda: mxq.mx_quant_live_rows(
             x, 2, h(2, dtype=torch.int32)),
         "live q": lambda: mxq.mx_quant_live_rows(x, 2, lc, q=h(T, H)),
@@ -140,6 +142,10 @@ def short_output_calls(g):
             x, ids, R, scales=g(R - 1, H // 128)),
         "scatter_ex q short": lambda: mxq.moe_scatter_quant_ex(
             x, ids, R, q=g(R - 1, H)),
+        "scatter_ex mfma scales short": lambda: mxq.moe_scatter_quant_ex(
+            x, ids, R, scale_layout="mfma16", scales=g(255)),
+        "live_ex mfma scales short": lambda: mxq.mx_quant_live_rows_ex(
+            x, 2, lc, scale_layout="mfma32", scales=g(1, 1, 63, 4)),
         "live q narrow": lambda: mxq.mx_quant_live_rows(
             x, 2, lc, q=g(T, H - 16)),
         "live scales narrow": lambda: mxq.mx_quant_live_rows(

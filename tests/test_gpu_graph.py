@@ -249,3 +249,131 @@ def test_graph_replay_variants_upscale_weights(ora):
         assert_equal(host(wso_s), wso_ref, "weight scales")
         # eager work between replays
         _ = (x_s.float() * 2).sum().item()
+
+
+def test_graph_replay_psum_repack_and_placements(ora):
+    """The psum repack (m_indices from psum, expanded rows -> masked slab
+    with 4-byte scales, slab -> expanded rows with weights), the scatter of
+    quantized rows and the scatter with MFMA-placed scales, captured once
+    and replayed three times with new routings and psum counts (some over
+    the slab capacity); every replay is checked."""
+    from test_oracle_psum import build_layout
+    T, H, E, K, G = 300, 256, 12, 3, 32
+    R = ora.compact_row_bound(T * K, E, 128)
+    PE, align, max_m = 6, 128, 64
+    rows_cap = PE * align           # counts stay below align
+    ng = H // G
+    C = 0xA5
+    ids_s = torch.zeros((T, K), dtype=torch.int32, device=DEV)
+    x_s = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
+    lay_out = {k: torch.empty(shape, dtype=torch.int32, device=DEV)
+               for k, shape in (("counts", (E,)), ("expert_offsets", (E + 1,)),
+                                ("m_indices", (R,)), ("masked_m", (E,)),
+                                ("src2dst", (T, K)), ("overflow_flag", (1,)))}
+    ws = torch.empty(max(1, mxq.moe_layout_workspace_bytes(T, K, E)),
+                     dtype=torch.uint8, device=DEV)
+    q_s = torch.empty((R, H), dtype=torch.uint8, device=DEV)
+    sm_s = mxq.mfma_scales(R, H, 16, DEV)
+    qt_s = torch.zeros((T, H), dtype=torch.uint8, device=DEV)
+    st_s = torch.zeros((T, ng), dtype=torch.uint8, device=DEV)
+    qr_s = torch.empty((R, H), dtype=torch.uint8, device=DEV)
+    sr_s = torch.empty((R, ng), dtype=torch.uint8, device=DEV)
+    psum_s = torch.zeros(PE, dtype=torch.int32, device=DEV)
+    mi_s = torch.empty(rows_cap, dtype=torch.int32, device=DEV)
+    xe_s = torch.zeros((rows_cap, H), dtype=torch.bfloat16, device=DEV)
+    xsc_s = torch.zeros((rows_cap, 2), dtype=torch.float32, device=DEV)
+    slab_s = torch.empty((PE * max_m, H), dtype=torch.bfloat16, device=DEV)
+    slabsc_s = torch.empty((PE * max_m, 2), dtype=torch.float32, device=DEV)
+    w_s = torch.zeros(rows_cap, dtype=torch.float32, device=DEV)
+    eo_s = torch.empty((rows_cap, H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        lay = mxq.moe_layout(ids_s, 0, E, "compact", num_rows=R, out=lay_out,
+                             workspace=ws)
+        mxq.moe_scatter_quant_ex(x_s, lay["src2dst"], R, "e8m0_g32",
+                                 "no_clip", "mfma16", q=q_s, scales=sm_s)
+        mxq.moe_scatter_rows(qt_s, lay["src2dst"], R, scales=st_s, out=qr_s,
+                             out_scales=sr_s)
+        mxq.moe_m_indices_from_psum(psum_s, rows_cap, align, out=mi_s)
+        res = mxq.moe_expand_to_masked_slab(xe_s, psum_s, max_m, align,
+                                            scales=xsc_s, slab=slab_s,
+                                            slab_scales=slabsc_s)
+        mxq.moe_masked_slab_to_expand(slab_s, res[2], psum_s, max_m, align,
+                                      weights=w_s, out=eo_s)
+        return res
+
+    say("graph psum: warm-up on a side stream")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("graph psum: capture")
+    with torch.cuda.graph(g):
+        _, _, mm_s, flags_s = step()
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        rng = np.random.default_rng(4000 + rep)
+        ids = si.uniform_topk(rng, T, E + 4, K)      # some ids non-local
+        x = si.gaussian_bf16(rng, (T, H))
+        qt = si.random_e4m3_bytes(rng, (T, H))
+        st = rng.integers(0, 255, (T, ng)).astype(np.uint8)
+        counts = rng.integers(0, 100, PE)
+        counts[rep] = 0
+        _, psum, _, _ = build_layout(counts.tolist(), align, 1)
+        xe = si.gaussian_bf16(rng, (rows_cap, H))
+        xsc = rng.standard_normal((rows_cap, 2)).astype(np.float32)
+        w = rng.random(rows_cap).astype(np.float32)
+        ids_s.copy_(i32_to_dev(ids))
+        x_s.copy_(bf16_to_dev(x))
+        qt_s.copy_(u8_to_dev(qt))
+        st_s.copy_(u8_to_dev(st))
+        psum_s.copy_(i32_to_dev(psum))
+        xe_s.copy_(bf16_to_dev(xe))
+        xsc_s.copy_(f32_to_dev(xsc))
+        w_s.copy_(f32_to_dev(w))
+        for t in (q_s, sm_s, qr_s, sr_s, slab_s.view(torch.uint8),
+                  slabsc_s.view(torch.uint8), eo_s.view(torch.uint8)):
+            t.fill_(C)
+        mi_s.fill_(-7)
+        torch.cuda.synchronize()
+        say("graph psum: replay", rep, "counts", counts.tolist())
+        g.replay()
+        torch.cuda.synchronize()
+
+        ref = ora.moe_layout(ids, 0, E, "compact", num_rows=R)
+        s2d = ref["src2dst"]
+        assert_equal(host(lay_out["src2dst"]), s2d, "src2dst")
+        q_ref, s_rows = ora.scatter_quant_ex(
+            x, s2d, G, R, "ceil", "rows", q=np.full((R, H), C, np.uint8),
+            s=np.full((R, ng), C, np.uint8))
+        assert_equal(host(q_s), q_ref, "scatter fp8")
+        assert_equal(host(sm_s), ora.mfma_scales(s_rows, H, G, 16, fill=C),
+                     "MFMA-placed scales")
+        qr_ref, sr_ref = ora.scatter_rows(
+            qt, s2d, R, scales=st, out=np.full((R, H), C, np.uint8),
+            out_scales=np.full((R, ng), C, np.uint8))
+        assert_equal(host(qr_s), qr_ref, "scatter_rows")
+        assert_equal(host(sr_s), sr_ref, "scatter_rows scales")
+        assert_equal(host(mi_s), ora.m_indices_from_psum(psum, align,
+                                                         rows_cap),
+                     "m_indices")
+        slab_ref, slabsc_ref, mm_ref, fl_ref = ora.expand_to_masked_slab(
+            xe.view(np.uint8), psum, align, max_m, scales=xsc,
+            slab=np.full((PE * max_m, 2 * H), C, np.uint8),
+            slab_scales=np.full((PE * max_m, 2), C, np.uint8).view(
+                np.uint8).repeat(4, axis=1).view(np.float32))
+        assert_equal(host(slab_s.view(torch.uint8)), slab_ref, "slab")
+        assert_equal(host(slabsc_s).view(np.uint32),
+                     slabsc_ref.view(np.uint32), "slab scales")
+        assert_equal(host(mm_s), mm_ref, "masked_m")
+        assert int(host(flags_s)[0]) == fl_ref
+        eo_ref = ora.masked_slab_to_expand(
+            slab_ref.view(np.uint16), mm_ref, psum, align, max_m, weights=w,
+            out=np.full((rows_cap, H), C * 257, np.uint16))
+        assert_equal(bf16_to_host(eo_s), eo_ref, "slab to expanded")
+        # eager work between replays
+        _ = (x_s.float() * 2).sum().item()
