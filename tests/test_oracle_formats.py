@@ -153,7 +153,8 @@ def exact_scale_exponent(amax: float) -> int:
 
 def test_scale_exponent_every_positive_bf16(ora):
     """All 32639 positive finite bf16 values (and zero) against exact rational
-    arithmetic.  Also pins the unclamped range the survey reports."""
+    arithmetic.  Also pins the unclamped exponent range over bf16,
+    -141 ... 120, so the -127 clamp is live for tiny groups."""
     bits = np.arange(0, 0x7F80, dtype=np.uint32) << 16
     vals = f32_from_bits(bits).astype(np.float64)
     got = np.array([ora.pow2_scale_exponent(v) for v in vals])
