@@ -219,6 +219,13 @@ def main():
     cbuf_b = torch.empty_like(cbuf_a)
     copy_us = time_calls(torch, lambda: cbuf_b.copy_(cbuf_a), reps=10)
     copy_gbs = 2 * cbuf_a.numel() / (copy_us * 1e-6) / 1e9
+    # the same copy with the library's 16-byte vector copy kernel
+    copy16 = {}
+    for nt in (False, True):
+        us = time_calls(torch, lambda: mxq.mxq_copy16(cbuf_a, cbuf_b, nt),
+                        reps=10)
+        copy16["nontemporal" if nt else "plain"] = round(
+            2 * cbuf_a.numel() / (us * 1e-6) / 1e9, 1)
     del cbuf_a, cbuf_b
 
     def step():
@@ -334,6 +341,7 @@ def main():
         "algorithmic_bytes": {"moe_layout": B_lay, "moe_scatter_quant": B_sq,
                               "moe_combine": B_cb, "step": B_step},
         "box_copy_gbs": round(copy_gbs, 1),
+        "box_copy16_kernel_gbs": copy16,
         "roofline": {
             "bound": "hbm",
             "kernel": "moe_combine",

@@ -30,6 +30,7 @@ __all__ = [
     "mxq_abi_version", "moe_m_indices_from_psum", "moe_expand_to_masked_slab",
     "moe_masked_slab_to_expand", "moe_scatter_rows", "upscale_fp8_to_bf16",
     "requant_weight_block_ue8m0", "mxq_mfma_scale_bytes", "mfma_scales",
+    "mxq_copy16",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +88,7 @@ _SIGNATURES = {
                                       _i32, _p, _i64, _p, _i32, _i64, _p]),
     "mx_quant_live_rows_mfma": (_i32, [_p, _i64, _i32, _i64, _p, _i32, _i32,
                                        _i32, _p, _i64, _p, _i32, _p]),
+    "mxq_copy16": (_i32, [_p, _p, _i64, _i32, _p]),
     "mxq_status_string": (ctypes.c_char_p, [_i32]),
     "mxq_abi_version": (_i32, []),
 }
@@ -216,6 +218,22 @@ def requant_workspace_bytes(T: int, H: int) -> int:
 
 def mxq_abi_version() -> int:
     return int(lib().mxq_abi_version())
+
+
+def mxq_copy16(src: torch.Tensor, dst: torch.Tensor,
+               nontemporal: bool = False) -> torch.Tensor:
+    """Bandwidth reference: copy src's bytes into dst with the library's
+    16-byte vector copy kernel (see mxq.h).  Both contiguous, same size."""
+    _dev(src, "src")
+    _dev(dst, "dst", src)
+    if not (src.is_contiguous() and dst.is_contiguous()) or \
+            src.numel() * src.element_size() != dst.numel() * dst.element_size():
+        raise ValueError("src and dst must be contiguous and the same size")
+    st = lib().mxq_copy16(_ptr(src), _ptr(dst),
+                          src.numel() * src.element_size(), int(nontemporal),
+                          _stream(src))
+    _check("mxq_copy16", st)
+    return dst
 
 
 def mxq_mfma_scale_bytes(rows: int, H: int, tile_m: int = 32) -> int:

@@ -268,6 +268,16 @@ mxq_status mx_quant_live_rows_mfma(const void* x_bf16, int64_t ld_x,
                                    void* q_fp8, int64_t ld_q, void* scales,
                                    int32_t tile_m, void* stream);
 
+/* --------------------------------------------------------- diagnostics */
+
+/* Bandwidth reference, not a step of the path: copies `bytes` (a multiple of
+ * 16) from src to dst (both device, 16-byte aligned, not overlapping) with
+ * 16-byte vector loads and stores, four loads in flight per lane, stores
+ * non-temporal when `nontemporal` is nonzero.  Timing it beside the path's
+ * kernels gives the box's achievable copy rate. */
+mxq_status mxq_copy16(const void* src, void* dst, int64_t bytes,
+                      int32_t nontemporal, void* stream);
+
 /* ------------------------------------------------------------- requant */
 
 /* Per-token scaled fp8 -> one per-tensor scale [P2 impl. items 1-2].

@@ -141,6 +141,15 @@ def test_scatter_quant_ex_validation(mxq):
     assert call(rows=0, q=None, s=None, rs=4, c4=0) == 0
 
 
+def test_copy16_validation(mxq):
+    L = mxq.lib()
+    assert L.mxq_copy16(FAKE, FAKE + 4096, 0, 0, None) == 0
+    assert L.mxq_copy16(FAKE, FAKE + 4096, 24, 0, None) == INVALID
+    assert L.mxq_copy16(FAKE, FAKE + 4096, -16, 1, None) == INVALID
+    assert L.mxq_copy16(None, FAKE, 32, 0, None) == INVALID
+    assert L.mxq_copy16(FAKE + 8, FAKE + 4096, 32, 0, None) == INVALID
+
+
 def test_mfma_placement_validation(mxq):
     """The block-scaled MFMA placement: size query and entry-point checks
     (every rejected call returns before anything is enqueued)."""

@@ -115,6 +115,7 @@ def host_argument_calls(g):
         "upscale out": lambda: mxq.upscale_fp8_to_bf16(
             q, g(T, 2, dtype=torch.float32),
             out=h(T, H, dtype=torch.bfloat16)),
+        "copy16 dst": lambda: mxq.mxq_copy16(q, h(T, H)),
         "weight s_inv": lambda: mxq.requant_weight_block_ue8m0(
             g(128, 128), h(1, 1, dtype=torch.float32)),
         "weight q_out": lambda: mxq.requant_weight_block_ue8m0(
