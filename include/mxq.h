@@ -197,7 +197,7 @@ mxq_status moe_scatter_quant_ex(const void* x_bf16, int64_t ld_x, int64_t T,
 /* Scale placement read directly by gfx950's block-scaled MFMA
  * (v_mfma_scale_f32_32x32x64_f8f6f4 with tile_m = 32, or
  * v_mfma_scale_f32_16x16x128_f8f6f4 with tile_m = 16) when the quantized
- * rows are its A (or B) operand [P3 Review highlights item 3 and P4 impl.
+ * rows are its A operand [P3 Review highlights item 3 and P4 impl.
  * item 1: scales are stored the way the consuming GEMM reads them].  One
  * instruction covers a tile of tile_m rows by 64*32/tile_m channels; the
  * scale of its 32-channel block h (h < 64/tile_m) of row r is read from lane
