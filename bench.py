@@ -221,11 +221,11 @@ def main():
     copy_gbs = 2 * cbuf_a.numel() / (copy_us * 1e-6) / 1e9
     # the same copy with the library's 16-byte vector copy kernel
     copy16 = {}
-    for nt in (False, True):
-        us = time_calls(torch, lambda: mxq.mxq_copy16(cbuf_a, cbuf_b, nt),
+    for mode, name in ((0, "plain"), (1, "nontemporal_stores"),
+                       (3, "nontemporal_loads_and_stores")):
+        us = time_calls(torch, lambda: mxq.mxq_copy16(cbuf_a, cbuf_b, mode),
                         reps=10)
-        copy16["nontemporal" if nt else "plain"] = round(
-            2 * cbuf_a.numel() / (us * 1e-6) / 1e9, 1)
+        copy16[name] = round(2 * cbuf_a.numel() / (us * 1e-6) / 1e9, 1)
     del cbuf_a, cbuf_b
 
     def step():
@@ -291,6 +291,32 @@ def main():
     # host launch cost); reported beside the eager timed region
     graph_ms = graph_step_ms(torch, step, args.warmup, args.steps)
 
+    # The same step with the 256 MB last-level cache (MALL) and the L2s
+    # flushed before each step by reading 512 MB, so that every input comes
+    # from HBM (in the loop above the token rows stay cached from the
+    # previous step, since the combine's loads and stores bypass the
+    # cache); events bracket the step's kernels alone.
+    flush = torch.zeros(512 << 20, dtype=torch.uint8,
+                        device=dev).view(torch.float32)
+    n_cold = min(args.steps, 20)
+    evc = [torch.cuda.Event(enable_timing=True) for _ in range(4 * n_cold)]
+    torch.cuda.synchronize()
+    for i in range(n_cold):
+        flush.sum()
+        evc[4 * i].record(cur)
+        status |= L.moe_layout(*lay_args)
+        evc[4 * i + 1].record(cur)
+        status |= L.moe_scatter_quant(*sq_args)
+        evc[4 * i + 2].record(cur)
+        status |= L.moe_combine(*cb_args)
+        evc[4 * i + 3].record(cur)
+    torch.cuda.synchronize()
+    if status != 0:
+        raise RuntimeError("a library call in the flushed loop failed")
+    del flush
+    cold = [float(np.mean([evc[4 * i + k].elapsed_time(evc[4 * i + k + 1])
+                           for i in range(n_cold)])) for k in range(3)]
+
     value = B_step / (step_ms * 1e-3) / 1e9
     cb_gbs = B_cb / (np.mean(cb_ms) * 1e-3) / 1e9
     sq_gbs = B_sq / (np.mean(sq_ms) * 1e-3) / 1e9
@@ -340,6 +366,21 @@ def main():
                         "moe_combine": round(cb_gbs, 2)},
         "algorithmic_bytes": {"moe_layout": B_lay, "moe_scatter_quant": B_sq,
                               "moe_combine": B_cb, "step": B_step},
+        "step_mall_flushed": {
+            "note": "the MALL and L2s flushed (512 MB read) before each "
+                    "step; HIP events around the step's kernels; "
+                    "%d steps" % n_cold,
+            "ms_per_step": round(sum(cold), 4),
+            "gbs": round(B_step / (sum(cold) * 1e-3) / 1e9, 2),
+            "pct_of_peak": round(
+                100 * B_step / (sum(cold) * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+            "kernels_us": {"moe_layout": round(1e3 * cold[0], 2),
+                           "moe_scatter_quant": round(1e3 * cold[1], 2),
+                           "moe_combine": round(1e3 * cold[2], 2)},
+            "scatter_quant_plus_combine_pct_of_peak": round(
+                100 * (B_sq + B_cb) / ((cold[1] + cold[2]) * 1e-3) / 1e9 /
+                PEAK_HBM_GBS, 2),
+        },
         "box_copy_gbs": round(copy_gbs, 1),
         "box_copy16_kernel_gbs": copy16,
         "roofline": {

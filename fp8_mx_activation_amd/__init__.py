@@ -221,9 +221,10 @@ def mxq_abi_version() -> int:
 
 
 def mxq_copy16(src: torch.Tensor, dst: torch.Tensor,
-               nontemporal: bool = False) -> torch.Tensor:
+               nontemporal: int = 0) -> torch.Tensor:
     """Bandwidth reference: copy src's bytes into dst with the library's
-    16-byte vector copy kernel (see mxq.h).  Both contiguous, same size."""
+    16-byte vector copy kernel (see mxq.h).  Both contiguous, same size;
+    ``nontemporal`` bit 0 = non-temporal stores, bit 1 = loads."""
     _dev(src, "src")
     _dev(dst, "dst", src)
     if not (src.is_contiguous() and dst.is_contiguous()) or \

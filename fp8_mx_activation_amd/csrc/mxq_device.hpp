@@ -20,6 +20,16 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Non-temporal 16-byte load (global_load_dwordx4 ... nt) for data read
+// once: it does not displace cached lines.  On MI355X a gather of
+// read-once rows runs markedly faster with it than with plain loads.
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+  return u32x4{__builtin_nontemporal_load(s), __builtin_nontemporal_load(s + 1),
+               __builtin_nontemporal_load(s + 2),
+               __builtin_nontemporal_load(s + 3)};
+}
+
 __device__ __forceinline__ void store16(void* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }

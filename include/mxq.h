@@ -272,8 +272,9 @@ mxq_status mx_quant_live_rows_mfma(const void* x_bf16, int64_t ld_x,
 
 /* Bandwidth reference, not a step of the path: copies `bytes` (a multiple of
  * 16) from src to dst (both device, 16-byte aligned, not overlapping) with
- * 16-byte vector loads and stores, four loads in flight per lane, stores
- * non-temporal when `nontemporal` is nonzero.  Timing it beside the path's
+ * 16-byte vector loads and stores, four loads in flight per lane.
+ * `nontemporal` bit 0 makes the stores non-temporal, bit 1 the loads (values
+ * 0-3; others: MXQ_ERR_INVALID_ARGUMENT).  Timing it beside the path's
  * kernels gives the box's achievable copy rate. */
 mxq_status mxq_copy16(const void* src, void* dst, int64_t bytes,
                       int32_t nontemporal, void* stream);

@@ -148,6 +148,8 @@ def test_copy16_validation(mxq):
     assert L.mxq_copy16(FAKE, FAKE + 4096, -16, 1, None) == INVALID
     assert L.mxq_copy16(None, FAKE, 32, 0, None) == INVALID
     assert L.mxq_copy16(FAKE + 8, FAKE + 4096, 32, 0, None) == INVALID
+    assert L.mxq_copy16(FAKE, FAKE + 4096, 32, 4, None) == INVALID
+    assert L.mxq_copy16(FAKE, FAKE + 4096, 32, -1, None) == INVALID
 
 
 def test_mfma_placement_validation(mxq):

@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("nbytes", [16, 48, 4096 * 4 + 16, (1 << 20) + 48,
                                     64 << 20])
-@pytest.mark.parametrize("nt", [False, True])
+@pytest.mark.parametrize("nt", [0, 1, 2, 3])
 def test_copy16_copies_every_byte(nbytes, nt):
     g = torch.Generator(device=DEV).manual_seed(nbytes)
     src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV,
