@@ -544,7 +544,11 @@ def other_rows(torch, mxq, si, dev):
     s = torch.empty((R, d.H // 128), dtype=torch.uint8, device=dev)
     yv = si.gaussian_bf16_device(202, (R, d.H), dev)
     lay = mxq.moe_layout(ids, 0, 32, "masked", capacity=128)
-    loc = int(((d.topk_ids >= 0) & (d.topk_ids < 32)).sum())
+    loc_mask = (d.topk_ids >= 0) & (d.topk_ids < 32)
+    loc = int(loc_mask.sum())
+    touched_d = int(loc_mask.any(axis=1).sum())
+    b_sq_d = bytes_scatter(touched_d, d.T, d.K, d.H, 128, loc)
+    b_cb_d = bytes_combine(d.T, d.K, d.H, loc)
     us_l = time_calls(torch, lambda: mxq.moe_layout(
         ids, 0, 32, "masked", capacity=128, out=lay))
     us_s = time_calls(torch, lambda: mxq.moe_scatter_quant(
@@ -555,7 +559,10 @@ def other_rows(torch, mxq, si, dev):
                     "slab capacity 128, UE8M0 group-128",
         "local_assignments": loc, "layout_us": round(us_l, 2),
         "scatter_quant_us": round(us_s, 2), "combine_us": round(us_c, 2),
-        "assignments_per_s": round(loc / ((us_l + us_s + us_c) * 1e-6), 1)}
+        "assignments_per_s": round(loc / ((us_l + us_s + us_c) * 1e-6), 1),
+        "scatter_quant_bytes": b_sq_d, "combine_bytes": b_cb_d,
+        "note": "latency-bound: %.2f MB and %.2f MB move in the scatter and "
+                "the combine" % (b_sq_d / 1e6, b_cb_d / 1e6)}
 
     # send-side MX quant over live rows: 24576 x 7168 padded, 112 live
     xs = si.gaussian_bf16_device(404, (24576, 7168), dev)
