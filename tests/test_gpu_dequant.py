@@ -95,8 +95,11 @@ def run_weights(ora, q, s, inplace=False):
 
 
 @pytest.mark.parametrize("B,N,K", [(2, 256, 384), (3, 200, 272), (1, 1, 16),
-                                   (1, 129, 144), (4, 128, 128)])
+                                   (1, 129, 144), (4, 128, 128),
+                                   (2, 256, 1408), (1, 300, 2064)])
 def test_weight_requant_shapes(ora, B, N, K):
+    """Ragged rows and columns; 1408 and 2064 columns mix whole 1024-column
+    tiles with a partial one (and 300 rows a partial row band)."""
     q, s = si.block_weights(N * K + B, B, N, K)
     run_weights(ora, q, s)
 
