@@ -676,13 +676,25 @@ def other_rows(torch, mxq, si, dev):
     ou = torch.empty((rows_u, H_u), dtype=torch.bfloat16, device=dev)
     us = time_calls(torch, lambda: mxq.upscale_fp8_to_bf16(qu, su, n_u,
                                                           out=ou))
+    # the same calls writing three output buffers in turn (3 x 117 MB, more
+    # than the 256 MB MALL), so each call's output reaches HBM during the
+    # following calls instead of being overwritten in the cache
+    ous = [ou] + [torch.empty_like(ou) for _ in range(2)]
+    turn = [0]
+
+    def up_rot():
+        turn[0] += 1
+        mxq.upscale_fp8_to_bf16(qu, su, n_u, out=ous[turn[0] % 3])
+    us_rot = time_calls(torch, up_rot, reps=21)
     byts = n_u * (H_u + 4 * (H_u // 128) + 2 * H_u)
     rows["upscale"] = {
         "workload": "24576 x 7168 fp8 receive buffer, group-128 fp32 scales, "
                     "first 8192 rows upscaled to bf16",
         "us": round(us, 2), "algorithmic_bytes": byts,
-        "gbs": round(byts / (us * 1e-6) / 1e9, 2)}
-    del qu, su, ou
+        "gbs": round(byts / (us * 1e-6) / 1e9, 2),
+        "rotating_outputs_us": round(us_rot, 2),
+        "rotating_outputs_gbs": round(byts / (us_rot * 1e-6) / 1e9, 2)}
+    del qu, su, ou, ous
 
     # weight-side UE8M0 block requant of 32 local experts' gate/up and down
     # weights (load time)

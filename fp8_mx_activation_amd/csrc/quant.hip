@@ -81,7 +81,9 @@ __global__ __launch_bounds__(1024) void scatter_quant_kernel(
 
 // Send-side quant.  Segment g owns blocks [g*bps, (g+1)*bps); block i of a
 // segment handles its live rows i, i + bps, ...  The grid depends only on the
-// host arguments; blocks past the live count return at once.
+// host arguments; blocks past the live count return at once.  The fp8 rows
+// are written once, with streaming stores (all 24576 rows of the padded
+// buffer live: 101.6 us instead of 108 us with plain stores on MI355X).
 template <int G, int RULE, int PLACE>
 __global__ __launch_bounds__(1024) void live_rows_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, int64_t rps, int32_t bps,
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(1024) void live_rows_kernel(
       const u32x4 b = load16(xr + col + 8);
       int e;
       const u32x4 v = quant16<G, RULE>(a, b, e);
-      store16(q + row * ld_q + col, v);
+      store16_nt(q + row * ld_q + col, v);
       if (lead) {
         const uint8_t sb = (uint8_t)(e + 127);
         if constexpr (PLACE == kMfma) {
