@@ -289,7 +289,10 @@ mxq_status mxq_copy16(const void* src, void* dst, int64_t bytes,
  *                 amax = max_t fl(max_i |dec(q_in[t,i])| * s_t); S = 1 when
  *                 amax = 0.  q_out = e4m3(fl(fl(dec(q_in) * s_t) * fl(1/S))).
  *   workspace     >= requant_workspace_bytes(T, H) bytes, device.
- * Two kernels: a max pass, then the requant pass. */
+ * Two kernels: a max pass, then the requant pass.  The max pass skips rows
+ * whose bound fl(448 * s_t) cannot raise the maximum (the result is the
+ * same); NaN codes in q_in are outside this contract and give an
+ * unspecified S. */
 mxq_status requant_per_token_to_per_tensor(
     const void* q_in_fp8, int64_t ld_in, const float* token_scales, int64_t T,
     int32_t H, void* q_out_fp8, int64_t ld_out, float* tensor_scale,

@@ -54,6 +54,62 @@ def test_requant_ragged_in_place(ora):
     requant_both(ora, q2, s2)
 
 
+def fp8_rows_with_amax(rng, amax, H):
+    """e4m3 rows (torch's float32 cast) whose largest magnitude is about
+    amax[t]; amax[t] = 0 gives an all-zero row."""
+    T = amax.shape[0]
+    z = rng.standard_normal((T, H), dtype=np.float32)
+    m = np.abs(z).max(axis=1, keepdims=True)
+    m[m == 0] = 1.0
+    y = np.clip(z * (amax.astype(np.float32)[:, None] / m), -448.0, 448.0)
+    return torch.from_numpy(y.astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def test_requant_max_from_rows_below_the_top_scale(ora):
+    """The max pass reads a row only while its bound 448 * s_t can still
+    raise the maximum.  Here the rows with the largest scale hold small
+    values, so the maximum comes from rows with smaller scales, which the
+    pass must still read; blocks of 16 rows see different top scales."""
+    rng = np.random.default_rng(11)
+    T, H = 777, 100              # H % 16 != 0 (row stride 112): byte tail read
+    u = rng.integers(-8, 5, size=T)
+    s = np.exp2(u).astype(np.float32)
+    amax = np.where(u == 4, 0.5, 448.0)
+    q = fp8_rows_with_amax(rng, amax, H)
+    requant_both(ora, q, s, ld_pad=12)
+    # ties: bound of the 2^3 rows (3584) equals the value of the 2^4 rows
+    # that hold 224, and one 2^2 row holds the max of its block
+    amax = np.where(u == 4, 224.0, np.where(u == 3, 448.0, 300.0))
+    q = fp8_rows_with_amax(rng, amax, H)
+    requant_both(ora, q, s, ld_pad=12)
+
+
+def test_requant_non_power_of_two_scales(ora):
+    """Scales that are not powers of two and row maxima spread over the
+    whole e4m3 range: bounds of many distinct values, so both read phases
+    of the max pass select rows."""
+    rng = np.random.default_rng(12)
+    for T, H in ((1000, 64), (3001, 208), (16389, 32)):   # 16389: 17 rows/block
+        s = rng.uniform(0.25, 4.0, size=T).astype(np.float32)
+        amax = np.exp2(rng.uniform(-9.0, np.log2(448.0), size=T))
+        amax[rng.random(T) < 0.05] = 0.0
+        q = fp8_rows_with_amax(rng, amax, H)
+        requant_both(ora, q, s)
+
+
+def test_requant_more_rows_than_one_ranking_round(ora):
+    """T = 1.1M rows: each block of the max pass owns 1075 rows and ranks
+    them in two runs of at most 1024, carrying its maximum across."""
+    rng = np.random.default_rng(13)
+    T, H = 1_100_000, 16
+    u = rng.integers(-6, 3, size=T)
+    s = np.exp2(u).astype(np.float32)
+    amax = np.exp2(rng.uniform(0.0, np.log2(448.0), size=T))
+    q = fp8_rows_with_amax(rng, amax, H)
+    requant_both(ora, q, s)
+
+
 def test_requant_empty():
     say("requant T=0")
     q = torch.zeros((0, 64), dtype=torch.uint8, device=DEV)
