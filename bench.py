@@ -514,6 +514,54 @@ def scale_variant_rows(torch, mxq, x, src2dst, R, H, q, B_sq, A, dev):
     return out
 
 
+def expanded_psum(counts, align):
+    """psum of the expanded layout for per-expert counts: expert e starts at
+    the aligned end of expert e - 1.  Returns (psum int32, aligned total)."""
+    psum = np.zeros(len(counts), np.int32)
+    prev = 0
+    for e, c in enumerate(counts):
+        psum[e] = -(-prev // align) * align + int(c)
+        prev = int(psum[e])
+    return psum, int(-(-prev // align) * align)
+
+
+def psum_repack_prefill(torch, mxq, si, dev):
+    """The two repack copies at a prefill-sized slab: 32 experts, capacity
+    2048, counts uniform in [1024, 2048], 7168-wide rows."""
+    E, MM, H = 32, 2048, 7168
+    rng = np.random.default_rng(si.SEEDS["decode_masked"] + 7)
+    cnt = rng.integers(1024, 2049, size=E)
+    psum_h, total = expanded_psum(cnt, 128)
+    psum = torch.from_numpy(psum_h).to(dev)
+    xr = si.random_e4m3_bytes_device(si.SEEDS["fp8_dispatch"] + 1,
+                                     (total, H), dev)
+    xsc = torch.randint(100, 140, (total, H // 128), dtype=torch.uint8,
+                        device=dev)
+    slab = torch.empty((E * MM, H), dtype=torch.uint8, device=dev)
+    slab_s = torch.empty((E * MM, H // 128), dtype=torch.uint8, device=dev)
+    us_e = time_calls(torch, lambda: mxq.moe_expand_to_masked_slab(
+        xr, psum, MM, 128, scales=xsc, slab=slab, slab_scales=slab_s))
+    _, _, mm, _ = mxq.moe_expand_to_masked_slab(xr, psum, MM, 128, scales=xsc,
+                                                 slab=slab, slab_scales=slab_s)
+    del xr, xsc, slab, slab_s
+    ys = si.gaussian_bf16_device(207, (E * MM, H), dev)
+    w = torch.rand(total, device=dev)
+    out = torch.empty((total, H), dtype=torch.bfloat16, device=dev)
+    us_b = time_calls(torch, lambda: mxq.moe_masked_slab_to_expand(
+        ys, mm, psum, MM, 128, weights=w, out=out))
+    real = int(cnt.sum())
+    b_e = real * 2 * (H + H // 128) + E * 8
+    b_b = real * (2 * H * 2 + 4)
+    return {"workload": "%d real rows in %d (32 experts, 128-aligned) <-> "
+                        "slab [32, 2048, 7168]" % (real, total),
+            "expand_to_masked_slab_us": round(us_e, 2),
+            "expand_bytes": b_e,
+            "expand_gbs": round(b_e / (us_e * 1e-6) / 1e9, 2),
+            "masked_slab_to_expand_us": round(us_b, 2),
+            "slab_to_expand_bytes": b_b,
+            "slab_to_expand_gbs": round(b_b / (us_b * 1e-6) / 1e9, 2)}
+
+
 def scatter_rows_row(torch, mxq, x, src2dst, R, H, q, T, K, A, dev):
     """The psum prefill path: the same tokens already quantized by the
     sender (fp8 rows + 56 UE8M0 bytes) copied into the compact layout."""
@@ -630,14 +678,7 @@ def other_rows(torch, mxq, si, dev):
     # expanded rows with the top-k weights applied
     counts = mxq.moe_layout(ids, 0, 32, "masked", capacity=128)["counts"]
     cnt = counts.cpu().numpy().astype(np.int64)
-    starts = np.zeros(32, np.int64)
-    psum_h = np.zeros(32, np.int32)
-    prev = 0
-    for e in range(32):
-        starts[e] = -(-prev // 128) * 128
-        psum_h[e] = starts[e] + cnt[e]
-        prev = psum_h[e]
-    total = int(-(-prev // 128) * 128)
+    psum_h, total = expanded_psum(cnt, 128)
     psum = torch.from_numpy(psum_h).to(dev)
     xr = torch.randint(0, 255, (total, 7168), dtype=torch.uint8, device=dev)
     xsc = torch.randint(100, 140, (total, 56), dtype=torch.uint8, device=dev)
@@ -664,6 +705,9 @@ def other_rows(torch, mxq, si, dev):
         "masked_slab_to_expand_us": round(us_b, 2),
         "slab_to_expand_bytes": real * (2 * 7168 * 2 + 4),
         "m_indices_from_psum_us": round(us_m, 2)}
+    del xr, xsc, slab, slab_s, ys, oexp
+    rows["psum_repack"]["prefill_shape"] = psum_repack_prefill(torch, mxq, si,
+                                                               dev)
 
     # receive-side upscale: fp8 + group-128 fp32 scales -> bf16 over the
     # live rows of the 3072 x 8 padded receive buffer

@@ -69,17 +69,39 @@ __global__ __launch_bounds__(1024) void m_indices_from_psum_kernel(
 constexpr int kCopyThreads = 1024;
 constexpr int kVecPerThread = 8;  // 16-byte loads in flight per thread
 
-// Rows per block of the copy kernels: at least 8, and at most 64 blocks per
-// expert, so the grid stays bounded for large slab capacities.
-inline int64_t copy_rows_per_block(int32_t max_m) {
-  const int64_t r = ceil_div(max_m, 64);
-  return r < 8 ? 8 : r;
+// Launch shape of the copy kernels, from host arguments only.  The grid has
+// a block for every (expert, range of slab rows), most of them empty when
+// few rows are live, so:
+//   slabs of more than 4M 16-byte vectors: 1024-thread blocks of about 3584
+//   vectors (3.5 per thread, one round of loads);
+//   smaller (decode-sized) slabs: 256-thread blocks of about 1024 vectors,
+//   so the blocks of rows that do not exist launch fewer wavefronts;
+// and at most 1024 blocks per expert.  Measured on MI355X with 7168-wide
+// rows: 32 experts x 2048 slab rows, 50282 live, expand 129.8 us and
+// slab-to-expand 248.4 us (144.9 and 293.1 us with 1024-thread blocks of
+// 32 rows); 32 x 128 slab rows, 140 live, 6.4 and 7.7 us (6.5 and 9.2 us
+// with 1024-thread blocks of 8 rows).
+struct CopyShape {
+  int64_t rows_per_block;
+  int threads;
+};
+
+inline CopyShape copy_shape(int32_t E, int32_t max_m, int64_t vec_per_row) {
+  const int64_t v = vec_per_row > 0 ? vec_per_row : 1;
+  const bool small = (int64_t)E * max_m * v <= ((int64_t)4 << 20);
+  const int threads = small ? 256 : kCopyThreads;
+  int64_t rpb = (small ? 1024 : 3584) / v;
+  const int64_t floor_rows = ceil_div(max_m, 1024);
+  if (rpb < floor_rows) rpb = floor_rows;
+  if (rpb < 1) rpb = 1;
+  return {rpb, threads};
 }
 
 // Block (e, b) copies rows [b*rpb, (b+1)*rpb) of expert e's slab, limited to
 // the rows that exist.  The rows' 16-byte vectors are numbered and dealt
 // round-robin to the threads; each thread issues up to kVecPerThread loads
-// before its stores, so a block costs about one memory round trip.
+// before its stores, so a block of the sizes copy_shape picks costs about
+// one memory round trip.
 // Block 0 also writes masked_m and the flags for every expert.
 __global__ __launch_bounds__(kCopyThreads) void expand_to_slab_kernel(
     const uint8_t* __restrict__ x, int64_t ld_x, int64_t src_rows,
@@ -338,12 +360,13 @@ extern "C" mxq_status moe_expand_to_masked_slab(
          (xs_row_stride | xs_col_stride | ss_row_stride | ss_col_stride) % 4))
       return MXQ_ERR_INVALID_ARGUMENT;
   }
-  const int64_t rpb = copy_rows_per_block(max_m);
+  const CopyShape cs = copy_shape(E, max_m, row_bytes / 16);
+  const int64_t rpb = cs.rows_per_block;
   const int64_t blocks = (int64_t)E * ceil_div(max_m, rpb);
   if (blocks > INT32_MAX ||
       rpb * (row_bytes / 16 + scale_cols) > (int64_t)INT32_MAX / 2)
     return MXQ_ERR_UNSUPPORTED;
-  expand_to_slab_kernel<<<(unsigned)blocks, kCopyThreads, 0,
+  expand_to_slab_kernel<<<(unsigned)blocks, cs.threads, 0,
                           as_stream(stream)>>>(
       static_cast<const uint8_t*>(x), ld_x, src_rows, row_bytes,
       static_cast<const uint8_t*>(x_scales), xs_row_stride, xs_col_stride,
@@ -368,19 +391,20 @@ extern "C" mxq_status moe_masked_slab_to_expand(
   if (!aligned16(slab_bf16) || (ld_slab * 2) % 16 != 0 || ld_slab < H ||
       !aligned16(out_bf16) || (ld_out * 2) % 16 != 0 || ld_out < H)
     return MXQ_ERR_INVALID_ARGUMENT;
-  const int64_t rpb = copy_rows_per_block(max_m);
+  const CopyShape cs = copy_shape(E, max_m, H / 8);
+  const int64_t rpb = cs.rows_per_block;
   const int64_t blocks = (int64_t)E * ceil_div(max_m, rpb);
   if (blocks > INT32_MAX || rpb * (H / 8) > (int64_t)INT32_MAX / 2)
     return MXQ_ERR_UNSUPPORTED;
   const uint16_t* sl = static_cast<const uint16_t*>(slab_bf16);
   uint16_t* o = static_cast<uint16_t*>(out_bf16);
   if (weights != nullptr)
-    slab_to_expand_kernel<true><<<(unsigned)blocks, kCopyThreads, 0,
+    slab_to_expand_kernel<true><<<(unsigned)blocks, cs.threads, 0,
                                   as_stream(stream)>>>(
         sl, ld_slab, H, masked_m, psum, align, max_m, (int32_t)rpb, weights,
         o, ld_out, out_rows);
   else
-    slab_to_expand_kernel<false><<<(unsigned)blocks, kCopyThreads, 0,
+    slab_to_expand_kernel<false><<<(unsigned)blocks, cs.threads, 0,
                                    as_stream(stream)>>>(
         sl, ld_slab, H, masked_m, psum, align, max_m, (int32_t)rpb, nullptr,
         o, ld_out, out_rows);
