@@ -157,3 +157,29 @@ def test_decode_shape(ora):
                                                  np.uint8)
     slab_case(ora, lay["counts"].tolist(), 128, 128, 7168, payload="fp8",
               scales=sc)
+
+
+def test_prefill_sized_slab(ora):
+    """Slabs of more than 4M 16-byte vectors, so both copies take their
+    large-slab launch shape (1024-thread blocks of about 3584 vectors):
+    12 experts, capacity 1024, one empty expert and one over capacity."""
+    rng = np.random.default_rng(21)
+    counts = rng.integers(300, 1025, size=12).tolist()
+    counts[3], counts[7] = 1100, 0
+    align, max_m = 128, 1024
+
+    def sc(total):
+        return np.random.default_rng(22).integers(100, 140, (total, 56),
+                                                  np.uint8)
+    # fp8 rows of 7168: 12 * 1024 * 448 vectors
+    slab_case(ora, counts, align, max_m, 7168, payload="fp8", scales=sc)
+    # bf16 rows of 4096: 12 * 1024 * 512 vectors, then back with weights
+    slab, mm, psum, total = slab_case(ora, counts, align, max_m, 4096)
+    w = np.random.default_rng(23).uniform(0.01, 1, total).astype(np.float32)
+    out0 = np.full((total, 4096), 0x1234, np.uint16)
+    got = mxq.moe_masked_slab_to_expand(
+        slab, mm, i32(psum), max_m, align,
+        weights=torch.from_numpy(w).to(DEV), out=bf16_to_dev(out0))
+    ref = ora.masked_slab_to_expand(bf16_to_host(slab), host(mm), psum, align,
+                                    max_m, weights=w, out=out0.copy())
+    assert_equal(bf16_to_host(got), ref, "weighted expand, large slab")
