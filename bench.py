@@ -602,12 +602,22 @@ def other_rows(torch, mxq, si, dev):
     us_s = time_calls(torch, lambda: mxq.moe_scatter_quant(
         x, lay["src2dst"], R, q=q, scales=s))
     us_c = time_calls(torch, lambda: mxq.moe_combine(yv, lay["src2dst"], w))
+
+    def layout_then_scatter():
+        mxq.moe_layout(ids, 0, 32, "masked", capacity=128, out=lay)
+        mxq.moe_scatter_quant(x, lay["src2dst"], R, q=q, scales=s)
+    us_ls = time_calls(torch, layout_then_scatter)
+    us_f = time_calls(torch, lambda: mxq.moe_layout_scatter_quant(
+        ids, x, 0, 32, "masked", capacity=128, out=lay, q=q, scales=s))
     rows["decode_masked"] = {
         "workload": "T=128, hidden 7168, experts [0,32) of 256 local, top-8, "
                     "slab capacity 128, UE8M0 group-128",
         "local_assignments": loc, "layout_us": round(us_l, 2),
         "scatter_quant_us": round(us_s, 2), "combine_us": round(us_c, 2),
+        "layout_then_scatter_quant_us": round(us_ls, 2),
+        "fused_layout_scatter_quant_us": round(us_f, 2),
         "assignments_per_s": round(loc / ((us_l + us_s + us_c) * 1e-6), 1),
+        "assignments_per_s_fused": round(loc / ((us_f + us_c) * 1e-6), 1),
         "scatter_quant_bytes": b_sq_d, "combine_bytes": b_cb_d,
         "note": "latency-bound: %.2f MB and %.2f MB move in the scatter and "
                 "the combine" % (b_sq_d / 1e6, b_cb_d / 1e6)}

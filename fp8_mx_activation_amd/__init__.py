@@ -30,7 +30,7 @@ __all__ = [
     "mxq_abi_version", "moe_m_indices_from_psum", "moe_expand_to_masked_slab",
     "moe_masked_slab_to_expand", "moe_scatter_rows", "upscale_fp8_to_bf16",
     "requant_weight_block_ue8m0", "mxq_mfma_scale_bytes", "mfma_scales",
-    "mxq_copy16",
+    "mxq_copy16", "moe_layout_scatter_quant",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -89,6 +89,10 @@ _SIGNATURES = {
     "mx_quant_live_rows_mfma": (_i32, [_p, _i64, _i32, _i64, _p, _i32, _i32,
                                        _i32, _p, _i64, _p, _i32, _p]),
     "mxq_copy16": (_i32, [_p, _p, _i64, _i32, _p]),
+    "moe_layout_scatter_quant": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _i64, _p, _p, _p, _p, _p, _p, _p,
+                                        _i64, _i32, _i32, _p, _i64, _p, _i64,
+                                        _p]),
     "mxq_status_string": (ctypes.c_char_p, [_i32]),
     "mxq_abi_version": (_i32, []),
 }
@@ -247,6 +251,41 @@ def mxq_mfma_scale_bytes(rows: int, H: int, tile_m: int = 32) -> int:
 
 # ------------------------------------------------------------------- layout
 
+def _layout_outputs(ids: torch.Tensor, E: int, num_rows: int,
+                    m_indices: bool, out: dict | None) -> dict:
+    """The layout's output tensors: those given in ``out`` (checked) or new
+    ones on the ids' device."""
+    T, K = ids.shape
+    o = dict(out or {})
+
+    def get(key, shape):
+        t = o.get(key)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.int32, device=ids.device)
+        else:
+            _dev(t, "out[%r]" % key, ids)
+            if t.dtype != torch.int32 or tuple(t.shape) != tuple(shape) or \
+                    not t.is_contiguous():
+                raise ValueError("out[%r] must be contiguous int32 %s"
+                                 % (key, shape))
+        return t
+
+    return dict(counts=get("counts", (E,)),
+                expert_offsets=get("expert_offsets", (E + 1,)),
+                m_indices=get("m_indices", (num_rows,)) if m_indices else None,
+                masked_m=get("masked_m", (E,)),
+                src2dst=get("src2dst", (T, K)),
+                overflow_flag=get("overflow_flag", (1,)),
+                num_rows=num_rows)
+
+
+def _layout_ids(topk_ids: torch.Tensor) -> torch.Tensor:
+    _dev(topk_ids, "topk_ids")
+    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
+        raise TypeError("topk_ids must be int32 [T, K]")
+    return topk_ids.contiguous()
+
+
 def moe_layout(topk_ids: torch.Tensor, expert_begin: int,
                num_local_experts: int, kind: str = "compact",
                block_e: int = 128, capacity: int = 0,
@@ -258,53 +297,77 @@ def moe_layout(topk_ids: torch.Tensor, expert_begin: int,
     ``m_indices`` (or None), ``masked_m``, ``src2dst``, ``overflow_flag``
     (device tensors) and ``num_rows``.  ``out`` may hold preallocated tensors
     under the same keys."""
-    _dev(topk_ids, "topk_ids")
-    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
-        raise TypeError("topk_ids must be int32 [T, K]")
-    ids = topk_ids.contiguous()
+    ids = _layout_ids(topk_ids)
     T, K = ids.shape
     E = num_local_experts
     k = LAYOUT_KINDS[kind]
     if num_rows is None:
         num_rows = (moe_compact_row_bound(T * K, E, block_e) if k == 0
                     else E * capacity)
-    dev = ids.device
-    o = dict(out or {})
-
-    def get(key, shape):
-        t = o.get(key)
-        if t is None:
-            t = torch.empty(shape, dtype=torch.int32, device=dev)
-        else:
-            _dev(t, "out[%r]" % key, ids)
-            if t.dtype != torch.int32 or tuple(t.shape) != tuple(shape) or \
-                    not t.is_contiguous():
-                raise ValueError("out[%r] must be contiguous int32 %s"
-                                 % (key, shape))
-        return t
-
-    counts = get("counts", (E,))
-    offsets = get("expert_offsets", (E + 1,))
-    m_idx = get("m_indices", (num_rows,)) if m_indices else None
-    masked_m = get("masked_m", (E,))
-    src2dst = get("src2dst", (T, K))
-    flag = get("overflow_flag", (1,))
+    lay = _layout_outputs(ids, E, num_rows, m_indices, out)
     need = moe_layout_workspace_bytes(T, K, E)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8,
+                                device=ids.device)
     else:
         _dev(workspace, "workspace", ids)
         if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor")
     st = lib().moe_layout(_ptr(ids), T, K, expert_begin, E, k, block_e,
-                          capacity, num_rows, _ptr(counts), _ptr(offsets),
-                          _ptr(m_idx), _ptr(masked_m), _ptr(src2dst),
-                          _ptr(flag), _ptr(workspace), workspace.numel(),
-                          _stream(ids))
+                          capacity, num_rows, _ptr(lay["counts"]),
+                          _ptr(lay["expert_offsets"]), _ptr(lay["m_indices"]),
+                          _ptr(lay["masked_m"]), _ptr(lay["src2dst"]),
+                          _ptr(lay["overflow_flag"]), _ptr(workspace),
+                          workspace.numel(), _stream(ids))
     _check("moe_layout", st)
-    return dict(counts=counts, expert_offsets=offsets, m_indices=m_idx,
-                masked_m=masked_m, src2dst=src2dst, overflow_flag=flag,
-                num_rows=num_rows)
+    return lay
+
+
+def moe_layout_scatter_quant(topk_ids: torch.Tensor, x: torch.Tensor,
+                             expert_begin: int, num_local_experts: int,
+                             kind: str = "compact", block_e: int = 128,
+                             capacity: int = 0, num_rows: int | None = None,
+                             fmt: str = "ue8m0_g128", m_indices: bool = True,
+                             out: dict | None = None,
+                             q: torch.Tensor | None = None,
+                             scales: torch.Tensor | None = None):
+    """``moe_layout`` and ``moe_scatter_quant`` in one launch, for routings
+    of at most 4096 assignments.  Returns ``(layout dict, q, scales)`` with
+    the same contents as the two calls."""
+    ids = _layout_ids(topk_ids)
+    T, K = ids.shape
+    E = num_local_experts
+    k = LAYOUT_KINDS[kind]
+    if num_rows is None:
+        num_rows = (moe_compact_row_bound(T * K, E, block_e) if k == 0
+                    else E * capacity)
+    lay = _layout_outputs(ids, E, num_rows, m_indices, out)
+    _dev(x, "x", ids)
+    code, G = SCALE_FORMATS[fmt]
+    ld_x = _rows(x, "x", (torch.bfloat16,))
+    if x.shape[0] != T:
+        raise ValueError("x must have one row per token of topk_ids")
+    H = x.shape[1]
+    if q is None:
+        q = _empty_rows_u8(num_rows, H, x.device)
+    if scales is None:
+        scales = torch.empty((num_rows, H // G), dtype=torch.uint8,
+                             device=x.device)
+    _dev(q, "q", x)
+    _dev(scales, "scales", x)
+    qq, ss = _u8(q), _u8(scales)
+    ld_q = _rows(qq, "q", (torch.uint8,))
+    ld_s = _rows(ss, "scales", (torch.uint8,))
+    _at_least(qq, "q", num_rows, H)
+    _at_least(ss, "scales", num_rows, H // G)
+    st = lib().moe_layout_scatter_quant(
+        _ptr(ids), T, K, expert_begin, E, k, block_e, capacity, num_rows,
+        _ptr(lay["counts"]), _ptr(lay["expert_offsets"]),
+        _ptr(lay["m_indices"]), _ptr(lay["masked_m"]), _ptr(lay["src2dst"]),
+        _ptr(lay["overflow_flag"]), _ptr(x), ld_x, H, code, _ptr(qq), ld_q,
+        _ptr(ss), ld_s, _stream(ids))
+    _check("moe_layout_scatter_quant", st)
+    return lay, q, scales
 
 
 def moe_read_overflow(overflow_flag: torch.Tensor) -> int:

@@ -175,6 +175,30 @@ mxq_status moe_scatter_quant(const void* x_bf16, int64_t ld_x, int64_t T,
                              uint8_t* scales, int64_t ld_s, int64_t num_rows,
                              void* stream);
 
+/* moe_layout followed by moe_scatter_quant in one launch, for routings of
+ * at most 4096 assignments (decode batches) [P2 impl. items 1-2: the
+ * low-latency decode dispatch; P1 impl. item 3: quant fused with the
+ * scatter].  One block per token ranks its own assignments from per-expert
+ * counts of the whole routing, so no separate layout launch is needed.
+ *
+ * Arguments are those of moe_layout (no workspace) followed by those of
+ * moe_scatter_quant (x_bf16 [T, ld_x], H, fmt, q_fp8 [num_rows, ld_q],
+ * scales [num_rows, ld_s], row-major scale bytes, exponent rule of
+ * moe_scatter_quant).  Every output (counts, expert_offsets, m_indices,
+ * masked_m, src2dst, overflow_flag, q, scales) is byte-identical to the two
+ * calls; rows that are no destination are not written.  A token's row may be
+ * read even when none of its experts is local.
+ * Errors: those of the two calls; T*K > 4096 is MXQ_ERR_UNSUPPORTED (use the
+ * two calls).  T = 0 runs the layout alone. */
+mxq_status moe_layout_scatter_quant(
+    const int32_t* topk_ids, int64_t T, int32_t K, int32_t expert_begin,
+    int32_t num_local_experts, mxq_layout_kind kind, int32_t block_e,
+    int32_t capacity, int64_t num_rows, int32_t* counts,
+    int32_t* expert_offsets, int32_t* m_indices, int32_t* masked_m,
+    int32_t* src2dst, int32_t* overflow_flag, const void* x_bf16,
+    int64_t ld_x, int32_t H, mxq_scale_fmt fmt, void* q_fp8, int64_t ld_q,
+    uint8_t* scales, int64_t ld_s, void* stream);
+
 /* moe_scatter_quant with a choice of exponent rule and of scale placement
  * [P3 impl. item 3 and Review highlights item 3: consumers read scales
  * column-major with four UE8M0 bytes packed per 32-bit word].  Scale byte g

@@ -120,6 +120,13 @@ def host_argument_calls(g):
             g(128, 128), h(1, 1, dtype=torch.float32)),
         "weight q_out": lambda: mxq.requant_weight_block_ue8m0(
             g(128, 128), g(1, 1, dtype=torch.float32), q_out=h(128, 128)),
+        "fused x": lambda: mxq.moe_layout_scatter_quant(
+            ids, h(T, H, dtype=torch.bfloat16), 0, 4, "masked", capacity=2),
+        "fused q": lambda: mxq.moe_layout_scatter_quant(
+            ids, x, 0, 4, "masked", capacity=2, q=h(R, H)),
+        "fused out": lambda: mxq.moe_layout_scatter_quant(
+            ids, x, 0, 4, "masked", capacity=2,
+            out={"src2dst": h(T, K, dtype=torch.int32)}),
     }
 
 
@@ -173,6 +180,13 @@ def short_output_calls(g):
         "upscale out short": lambda: mxq.upscale_fp8_to_bf16(
             q, g(T, 2, dtype=torch.float32),
             out=g(T - 1, H, dtype=torch.bfloat16)),
+        "fused q short": lambda: mxq.moe_layout_scatter_quant(
+            ids, x, 0, 4, "masked", capacity=2, q=g(R - 1, H)),
+        "fused scales narrow": lambda: mxq.moe_layout_scatter_quant(
+            ids, x, 0, 4, "masked", capacity=2, scales=g(R, H // 128 - 1)),
+        "fused x rows": lambda: mxq.moe_layout_scatter_quant(
+            ids, g(T - 1, H, dtype=torch.bfloat16), 0, 4, "masked",
+            capacity=2),
     }
 
 
