@@ -110,6 +110,14 @@ def test_requant_more_rows_than_one_ranking_round(ora):
     requant_both(ora, q, s)
 
 
+def test_requant_operation_order_cases(ora):
+    """Rows where two other operation orders round to other bytes than R6's
+    (built in test_oracle_paths): the kernel gives R6's bytes."""
+    from test_oracle_paths import requant_order_cases
+    q, scales, _, _ = requant_order_cases()
+    requant_both(ora, q, scales)
+
+
 def test_requant_empty():
     say("requant T=0")
     q = torch.zeros((0, 64), dtype=torch.uint8, device=DEV)

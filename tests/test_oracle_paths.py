@@ -146,6 +146,87 @@ def test_requant_properties(ora):
     assert (np.abs(y - x) <= tol).all()
 
 
+def test_requant_bytes_equal_an_independent_construction(ora):
+    """R6 built with other tools: torch's e4m3 decode, numpy float32
+    products in the stated order (dec(q) * s_t, then * fl(1/S) with
+    S = fl(amax / 448)), and torch's float32 -> e4m3fn cast, which rounds to
+    nearest even and agrees with the saturating encoder below 464 (every
+    |y| here is at most 448 (1 + 2^-23)).  Power-of-two scales, scales
+    spread over 2^-30 .. 2^30, and scales that are not powers of two."""
+    rng = np.random.default_rng(41)
+    for T, H, lo, hi in ((300, 512, -8.0, 4.0), (200, 96, -30.0, 30.0)):
+        q, s = si.per_token_fp8(rng, T, H, log2_lo=lo, log2_hi=hi)
+        s_np2 = (s * rng.uniform(0.5, 2.0, T)).astype(np.float32)
+        for sc in (s, s_np2):
+            out, S = ora.requant_per_token_to_per_tensor(q, sc)
+            d = torch.from_numpy(q).view(torch.float8_e4m3fn).float().numpy()
+            rq = d * sc[:, None]                      # float32 products
+            S_ref = np.float32(np.abs(rq).max()) / np.float32(448.0)
+            inv = np.float32(1.0) / S_ref
+            y = rq * inv
+            assert y.dtype == np.float32 and np.abs(y).max() < 464.0
+            ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(
+                torch.uint8).numpy()
+            assert np.float32(S) == S_ref
+            assert np.array_equal(out, ref)
+
+
+def e4m3_cast(y):
+    return torch.from_numpy(np.ascontiguousarray(y, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def requant_order_cases():
+    """Rows on which R6's order, fl(fl(dec * s_t) * fl(1/S)), and two
+    plausible other orders, dec * fl(s_t * fl(1/S)) and fl(dec * s_t) / S,
+    round to different e4m3 bytes.  Row 0 holds 448 with the largest scale
+    s0, which fixes S; every other row holds one code d (then -0 and zeros)
+    with a scale a few ulps from m * S / d, m an e4m3 midpoint, where a
+    one-ulp change of y can cross the midpoint.  Returns (q, scales, S,
+    stated-order bytes of column 0 of rows 1..)."""
+    codes = np.arange(0x01, 0x7F, dtype=np.uint8)
+    d = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    vals = torch.arange(0, 0x7F, dtype=torch.uint8).view(
+        torch.float8_e4m3fn).float().numpy()
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    mids = mids[(mids >= 1.0) & (mids < 440.0)]
+    s0 = np.float32(3.1)
+    S = np.float32(np.float32(448.0) * s0) / np.float32(448.0)
+    inv = np.float32(1.0) / S
+    k = np.arange(-16, 17).astype(np.float32) * np.float32(2.0 ** -23)
+    D = np.broadcast_to(d[:, None, None], (d.size, mids.size, k.size))
+    sc = (mids[None, :, None] * S / d[:, None, None] *
+          (1 + k[None, None, :])).astype(np.float32)
+    D, sc = D.ravel(), sc.ravel()
+    keep = D * sc < np.float32(448.0) * s0 * np.float32(0.999)
+    D, sc = D[keep], sc[keep]
+    rq = D * sc
+    ref = e4m3_cast(rq * inv)
+    diff_a = ref != e4m3_cast(D * (sc * inv))
+    diff_b = ref != e4m3_cast(rq / S)
+    assert diff_a.sum() >= 64 and diff_b.sum() >= 64
+    pick = np.concatenate([np.flatnonzero(diff_a)[:64],
+                           np.flatnonzero(diff_b)[:64]])
+    code_of = dict(zip(d.tolist(), codes.tolist()))
+    q = np.zeros((1 + pick.size, 16), np.uint8)
+    q[0, 0] = 0x7E
+    q[1:, 0] = [code_of[float(v)] for v in D[pick]]
+    q[1:, 1] = 0x80                                        # -0 stays -0
+    scales = np.concatenate([[s0], sc[pick]]).astype(np.float32)
+    return q, scales, S, ref[pick]
+
+
+def test_requant_operation_order_is_pinned(ora):
+    """The oracle follows R6's order on rows where two other orders give
+    other bytes (requant_order_cases)."""
+    q, scales, S, want = requant_order_cases()
+    out, S_got = ora.requant_per_token_to_per_tensor(q, scales)
+    assert np.float32(S_got) == S
+    assert np.array_equal(out[1:, 0], want)
+    assert (out[1:, 1] == 0x80).all() and out[0, 0] == 0x7E
+    assert (out[1:, 2:] == 0).all()
+
+
 def test_requant_zero_input(ora):
     q = np.zeros((4, 64), np.uint8)
     q[1] = 0x80
