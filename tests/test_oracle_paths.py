@@ -281,6 +281,56 @@ def test_combine_one_hot_and_empty_tokens(ora):
     assert np.isfinite(bf16_vals(out)).all()
 
 
+def f32_nearest(fr):
+    """The float32 nearest to the exact rational fr (ties to even),
+    returned as a Python float; |fr| < 2^100 here, so no overflow."""
+    from fractions import Fraction
+    if fr == 0:
+        return 0.0
+    neg = fr < 0
+    a = -fr if neg else fr
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                  # 2^e <= a < 2^(e+1)
+    q = max(e - 23, -149)                       # 24-bit significand
+    m = a / Fraction(2) ** q
+    n = m.numerator // m.denominator
+    r = m - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = float(n) * 2.0 ** q
+    return -v if neg else v
+
+
+def test_combine_fp32_order_equals_exact_fma(ora):
+    """R7 built independently: each fused multiply-add w * y + acc computed
+    exactly in rationals and rounded once to float32 (nearest, ties to
+    even), over j ascending from +0, skipping assignments without a row.
+    Multiply-then-add (two roundings) or j descending, planted in the
+    oracle, fail here."""
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    T, K, H, E = 24, 8, 32, 16
+    ids = si.uniform_topk(rng, T, E + 4, K)         # some ids non-local
+    lay = ora.moe_layout(ids, 0, E, "compact")
+    y = si.gaussian_bf16(rng, (lay["num_rows"], H))
+    w = si.softmax_weights(rng, T, K)
+    acc = ora.combine_f32(y, lay["src2dst"], w)
+    yv = bf16_vals(y)
+    want = np.zeros((T, H), np.float32)
+    for t in range(T):
+        for h in range(H):
+            a = 0.0
+            for j in range(K):
+                d = lay["src2dst"][t, j]
+                if d < 0:
+                    continue
+                a = f32_nearest(Fraction(float(w[t, j])) *
+                                Fraction(float(yv[d, h])) + Fraction(a))
+            want[t, h] = a
+    assert np.array_equal(want.view(np.uint32), acc.view(np.uint32))
+
+
 def test_combine_vs_float64(ora):
     b = si.tiny()
     lay = ora.moe_layout(b.topk_ids, 0, 8, "compact")
