@@ -670,16 +670,26 @@ def other_rows(torch, mxq, si, dev):
     byts = 2 * qi.numel() + qi.shape[0] * 4 + 4
     us_cold = time_calls_cold(torch, lambda: mxq.requant_per_token_to_per_tensor(
         qi, sc, q_out=qo, tensor_scale=Sd, workspace=rws), flush)
+    # worst case of the max pass: equal token scales, so no row can be
+    # skipped and pass 1 reads the whole input
+    sc_eq = torch.full_like(sc, 2.0 ** -3)
+    us_eq = time_calls(torch, lambda: mxq.requant_per_token_to_per_tensor(
+        qi, sc_eq, q_out=qo, tensor_scale=Sd, workspace=rws))
     rows["requant"] = {"workload": "16384 x 4096 fp8, per-token scales "
                                    "2^U, U~U[-8,4]",
                        "us": round(us, 2), "algorithmic_bytes": byts,
                        "gbs": round(byts / (us * 1e-6) / 1e9, 2),
                        "cold_us": round(us_cold, 2),
                        "cold_gbs": round(byts / (us_cold * 1e-6) / 1e9, 2),
+                       "equal_scales_us": round(us_eq, 2),
+                       "equal_scales_gbs": round(byts / (us_eq * 1e-6) / 1e9,
+                                                 2),
                        "note": "warm: the 64 MiB input stays in the 256 MB "
                                "MALL across the two passes and back-to-back "
                                "calls; cold: MALL flushed by reading 512 MB "
-                               "before each call"}
+                               "before each call; equal_scales: every token "
+                               "scale 2^-3, so the max pass cannot skip a "
+                               "row (warm)"}
     del qi, qo
 
     # psum (expanded) layout repack at the decode shape: the dispatcher's
