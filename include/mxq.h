@@ -242,9 +242,10 @@ mxq_status moe_scatter_quant_ex(const void* x_bf16, int64_t ld_x, int64_t T,
 int64_t mxq_mfma_scale_bytes(int64_t rows, int32_t H, int32_t tile_m);
 
 /* moe_scatter_quant_ex with the scales in the block-scaled MFMA placement
- * above: `scales` holds mxq_mfma_scale_bytes(num_rows, H, tile_m) bytes.
- * Errors as moe_scatter_quant_ex; tile_m other than 16 or 32 is
- * MXQ_ERR_INVALID_ARGUMENT. */
+ * above: `scales` holds mxq_mfma_scale_bytes(num_rows, H, tile_m) bytes and
+ * is 4-byte aligned (whole 32-bit words are written).  Errors as
+ * moe_scatter_quant_ex; tile_m other than 16 or 32, or an unaligned
+ * `scales`, is MXQ_ERR_INVALID_ARGUMENT. */
 mxq_status moe_scatter_quant_mfma(const void* x_bf16, int64_t ld_x, int64_t T,
                                   int32_t H, const int32_t* src2dst,
                                   int32_t K, mxq_scale_fmt fmt,

@@ -190,6 +190,7 @@ def test_mfma_placement_validation(mxq):
     assert call(T=0) == 0
     assert call(rows=0, q=None, s=None) == 0
     assert live(H=640, x=None) == INVALID
+    assert call(s=FAKE + 2) == INVALID          # scatter writes 32-bit words
 
 
 def test_upscale_and_weight_requant_validation(mxq):
