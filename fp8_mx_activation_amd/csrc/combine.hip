@@ -35,8 +35,13 @@ __global__ __launch_bounds__(1024) void combine_kernel(
     const int32_t* __restrict__ src2dst, const float* __restrict__ w,
     int32_t K, int32_t H, void* __restrict__ out, int64_t ld_out) {
   const int64_t t = blockIdx.x;
-  const int32_t* dl = src2dst + t * K;
-  const float* wl = w + t * K;
+  // lane j of every wavefront loads index and weight j (K <= 64) in one
+  // vector load each; readlane then gives them to the whole wavefront, so
+  // the row loads wait for one round trip, not one per assignment
+  const int lane = threadIdx.x & 63;
+  const int jl = min(lane, K - 1);
+  const int32_t d_lane = K > 0 ? src2dst[t * K + jl] : -1;
+  const int32_t w_lane = K > 0 ? __float_as_int(w[t * K + jl]) : 0;
   for (int col = threadIdx.x * 8; col < H; col += blockDim.x * 8) {
     float acc[8];
 #pragma unroll
@@ -48,9 +53,11 @@ __global__ __launch_bounds__(1024) void combine_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int j = j0 + u;
-        const int64_t d = j < K ? (int64_t)dl[j] : -1;
+        const int64_t d =
+            j < K ? (int64_t)__builtin_amdgcn_readlane(d_lane, j) : -1;
         ok[u] = d >= 0 && d < num_rows;
-        wt[u] = ok[u] ? wl[j] : 0.0f;
+        wt[u] = ok[u] ? __int_as_float(__builtin_amdgcn_readlane(w_lane, j))
+                      : 0.0f;
         v[u] = ok[u] ? load16_nt(y + d * ld_y + col) : u32x4{0, 0, 0, 0};
       }
 #pragma unroll

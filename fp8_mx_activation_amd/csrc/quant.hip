@@ -59,13 +59,13 @@ __global__ __launch_bounds__(1024) void scatter_quant_kernel(
     t = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     if (t >= T) return;
   }
-  const int32_t* dl = src2dst + t * K;
-  bool any = false;
-  for (int j = 0; j < K; ++j) {
-    const int64_t d = dl[j];
-    any |= (d >= 0 && d < num_rows);
-  }
-  if (!any) return;
+  // lane j of every wavefront loads destination j (K <= 64) in one vector
+  // load; a ballot tells whether the token has any, and readlane hands each
+  // writing wavefront its row, so the row loads wait for one round trip
+  const int lane = threadIdx.x & 63;
+  const int32_t d_lane = src2dst[t * K + min(lane, K - 1)];
+  const bool valid = lane < K && d_lane >= 0 && (int64_t)d_lane < num_rows;
+  if (__ballot(valid) == 0) return;  // the same in every wavefront
   const uint16_t* xr = x + t * ld_x;
   const bool lead = (threadIdx.x & (G / 16 - 1)) == 0;
   for (int col = threadIdx.x * 16; col < H; col += blockDim.x * 16) {
@@ -77,11 +77,10 @@ __global__ __launch_bounds__(1024) void scatter_quant_kernel(
     if (lead) row[H + col / G] = (uint8_t)(e + 127);
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
   const int ng = H / G;
   for (int j = threadIdx.x >> 6; j < K; j += nw) {
-    const int64_t d = dl[j];
+    const int64_t d = __builtin_amdgcn_readlane(d_lane, j);
     if (d < 0 || d >= num_rows) continue;
     uint8_t* qr = q + d * ld_q;
     for (int c = lane * 16; c < H; c += 64 * 16)
