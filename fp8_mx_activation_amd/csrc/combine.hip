@@ -8,14 +8,15 @@
 // j = 0..K-1 in order, skipping assignments without a row; the result is
 // rounded to bf16 (nearest even) or stored as fp32.
 //
-// One block per token; a lane owns 8 consecutive channels.  The K rows of a
-// token are loaded as independent 16-byte vectors before any arithmetic, so
-// each lane has up to eight loads in flight.  Per token the kernel reads
-// K valid rows of 2H bytes and writes one row.  Every expert-output row is
-// read exactly once, so the loads are non-temporal (measured on MI355X: the
-// prefill gather takes 183 us instead of 196 us with plain loads), and the
-// output row is written with streaming (non-temporal) stores so it does not
-// displace cached lines.
+// One block per token; a lane owns 8 consecutive channels.  The token's
+// indices and weights arrive in one vector load each (lane j holds entry j),
+// and the K rows are then loaded as independent 16-byte vectors before any
+// arithmetic, so each lane has up to eight loads in flight.  Per token the
+// kernel reads K valid rows of 2H bytes and writes one row.  Every
+// expert-output row is read exactly once, so the loads are non-temporal
+// (measured on MI355X: the prefill gather took 183 us instead of 196 us with
+// plain loads), and the output row is written with streaming (non-temporal)
+// stores so it does not displace cached lines.
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
 

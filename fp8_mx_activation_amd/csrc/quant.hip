@@ -31,9 +31,10 @@ enum Placement { kStrided = 0, kMfma = 1 };
 // followed by its scale bytes.  Writing whole rows per wavefront and
 // bypassing cache allocation for the write-once payload keeps the HBM write
 // stream sequential; the scale bytes use ordinary stores so partial lines
-// merge in L2.  Destinations come from src2dst (uniform per block: scalar
-// loads); a token without a destination in [0, num_rows) is skipped before
-// its row is read.
+// merge in L2.  Destinations come from src2dst in one vector load per
+// wavefront (lane j holds destination j, handed out with readlane); a token
+// without a destination in [0, num_rows) is skipped before its row is
+// read.
 //
 // MFMA placement.  A row's scale bytes go to one 32-bit word per (group of
 // four instructions, block within the instruction), words that the other
