@@ -132,10 +132,16 @@ __global__ __launch_bounds__(256) void requant_amax_kernel(
     const int n = (int)min((int64_t)kAmaxChunk, r_end - c0);
     uint32_t bnd[4];
     uint32_t bmax = 0;
+    // the four scales are loaded unconditionally (index clamped to the
+    // run's last row) so that they are in flight together
+    float sv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      sv[u] = sc[c0 + min((int)threadIdx.x + 256 * u, n - 1)];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = threadIdx.x + 256 * u;
-      bnd[u] = i < n ? __float_as_uint(448.0f * sc[c0 + i]) : 0u;
+      bnd[u] = i < n ? __float_as_uint(448.0f * sv[u]) : 0u;
       bmax = max(bmax, bnd[u]);
     }
     const uint32_t B = block_max4(bmax, red);
@@ -177,8 +183,18 @@ __global__ __launch_bounds__(256) void requant_apply_kernel(
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   __shared__ uint32_t red[4];
+  // the partials four per thread and round, loaded unconditionally (index
+  // clamped to the last one; a repeated partial leaves the maximum as it
+  // is) so that they are in flight together
   uint32_t m = 0;
-  for (int i = threadIdx.x; i < np; i += 256) m = max(m, partial[i]);
+  for (int i0 = 0; i0 < np; i0 += 4 * 256) {
+    uint32_t pv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      pv[u] = partial[min(i0 + (int)threadIdx.x + 256 * u, np - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m = max(m, pv[u]);
+  }
   m = wave_max(m);
   if (lane == 0) red[wv] = m;
   __syncthreads();
