@@ -325,9 +325,9 @@ def main():
     def step_fast(i):
         st = L.moe_layout(*lay_args)
         st |= L.moe_scatter_quant(*sq_args)
-        hev.record(2 * i, hs)
+        st |= hev.record(2 * i, hs)
         st |= L.moe_combine(*cb_args)
-        hev.record(2 * i + 1, hs)
+        st |= hev.record(2 * i + 1, hs)
         return st
 
     for _ in range(args.warmup):
@@ -352,13 +352,13 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        kev.record(4 * i, hs)
+        status |= kev.record(4 * i, hs)
         status |= L.moe_layout(*lay_args)
-        kev.record(4 * i + 1, hs)
+        status |= kev.record(4 * i + 1, hs)
         status |= L.moe_scatter_quant(*sq_args)
-        kev.record(4 * i + 2, hs)
+        status |= kev.record(4 * i + 2, hs)
         status |= L.moe_combine(*cb_args)
-        kev.record(4 * i + 3, hs)
+        status |= kev.record(4 * i + 3, hs)
     torch.cuda.synchronize()
     kev_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     if status != 0:
@@ -385,13 +385,13 @@ def main():
     torch.cuda.synchronize()
     for i in range(n_cold):
         flush.sum()
-        evc.record(4 * i, hs)
+        status |= evc.record(4 * i, hs)
         status |= L.moe_layout(*lay_args)
-        evc.record(4 * i + 1, hs)
+        status |= evc.record(4 * i + 1, hs)
         status |= L.moe_scatter_quant(*sq_args)
-        evc.record(4 * i + 2, hs)
+        status |= evc.record(4 * i + 2, hs)
         status |= L.moe_combine(*cb_args)
-        evc.record(4 * i + 3, hs)
+        status |= evc.record(4 * i + 3, hs)
     torch.cuda.synchronize()
     if status != 0:
         raise RuntimeError("a library call in the flushed loop failed")
