@@ -347,6 +347,19 @@ def main():
     hev.close()
     step_ms = wall_s * 1e3 / args.steps
 
+    # the same steps with no event at all, to show what the roofline's
+    # events cost the timed loop (reported beside value, not as value)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        status |= L.moe_layout(*lay_args)
+        status |= L.moe_scatter_quant(*sq_args)
+        status |= L.moe_combine(*cb_args)
+    torch.cuda.synchronize()
+    noev_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    if status != 0:
+        raise RuntimeError("a library call in the event-free pass failed")
+
     # per-kernel pass: the same steps with events around each kernel
     kev = HipEvents(4 * args.steps)
     torch.cuda.synchronize()
@@ -443,6 +456,7 @@ def main():
                   "every kernel",
         "moe_combine_us_in_timed_region": round(
             1e3 * float(np.mean(cb_ms)), 2),
+        "ms_per_step_without_events": round(noev_step_ms, 4),
         "scatter_quant_plus_combine": {
             "bytes": B_sq + B_cb,
             "us": round(1e3 * (np.mean(sq_ms) + np.mean(kcb_ms)), 2),
