@@ -209,11 +209,14 @@ __global__ __launch_bounds__(TK) void weight_requant_kernel(
     int64_t o_bs) {
   constexpr int CPR = TK / 16;  // chunks per tile row
   __shared__ uint32_t rmax[kWRowsPerPass][TK / kWBlock];
+  // consecutive blocks take consecutive 128-row blocks of one column tile
+  // (measured on MI355X at [32, 4096, 7168]: 324.9-329.6 us against
+  // 331.3-335.4 us with the column tiles of one row block consecutive)
   const int64_t blk = blockIdx.x;
-  const int32_t jt = (int32_t)(blk % ntk);
-  const int64_t t = blk / ntk;
-  const int32_t i = (int32_t)(t % nbn);
-  const int64_t b = t / nbn;
+  const int32_t i = (int32_t)(blk % nbn);
+  const int64_t t = blk / nbn;
+  const int32_t jt = (int32_t)(t % ntk);
+  const int64_t b = t / ntk;
   const int c = threadIdx.x % CPR;
   const int r = threadIdx.x / CPR;
   const int kb = c >> 3;                           // scale block in the tile
