@@ -5,19 +5,29 @@
 extern "C" int64_t moe_compact_row_bound(int64_t num_assignments,
                                          int32_t num_local_experts,
                                          int32_t block_e) {
-  // sglang PR #33128, key source snippets (_get_compact_all_tokens): each
-  // non-empty expert takes at least one block; the remaining assignments
-  // fill whole blocks.
+  // The largest padded row count any routing of A assignments over E
+  // experts can need (the static bound of sglang PR #33128 page, Key source
+  // snippets).  An expert with c > 0 assignments takes ceil(c / b) blocks:
+  // one block for its first assignment and floor((c - 1) / b) for the rest.
+  // With m non-empty experts the blocks therefore number at most
+  // m + floor((A - m) / b); raising m by one adds a block and removes at
+  // most one, so the worst case has as many non-empty experts as possible,
+  // m = min(A, E), and packs every remaining assignment into whole blocks.
   if (num_assignments < 0 || num_local_experts < 0 || block_e < 1) return -1;
-  const int64_t n = num_assignments < num_local_experts ? num_assignments
-                                                        : num_local_experts;
-  return (int64_t)block_e * (n + (num_assignments - n) / block_e);
+  const int64_t A = num_assignments;
+  const int64_t first_blocks = A < num_local_experts ? A : num_local_experts;
+  const int64_t rest_blocks = (A - first_blocks) / block_e;
+  return (int64_t)block_e * (first_blocks + rest_blocks);
 }
 
 extern "C" int32_t moe_should_use_masked(int32_t num_experts,
                                          int32_t num_local_experts) {
-  // sglang PR #33128, key source snippets (_should_use_masked_standard_layout)
-  return (num_experts > num_local_experts && num_local_experts <= 32) ? 1 : 0;
+  // Layout choice of sglang PR #33128 page, Key source snippets: the masked
+  // slab is chosen when experts are split across ranks (this rank holds a
+  // proper subset) and it holds at most 32 of them; otherwise compact.
+  const bool experts_split = num_experts > num_local_experts;
+  const bool few_local = num_local_experts <= 32;
+  return (experts_split && few_local) ? 1 : 0;
 }
 
 extern "C" size_t moe_layout_workspace_bytes(int64_t T, int32_t K, int32_t E) {

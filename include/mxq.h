@@ -86,7 +86,10 @@ typedef enum { MXQ_OUT_BF16 = 0, MXQ_OUT_F32 = 1 } mxq_out_dtype;
 
 /* Static row count of the compact layout that no routing can exceed
  * [P1 Key source snippets, _get_compact_all_tokens]:
- *   block_e * (n + (A - n) / block_e), n = min(A, E).
+ *   block_e * (n + (A - n) / block_e), n = min(A, E):
+ * each non-empty expert takes one block for its first assignment, so the
+ * worst case has min(A, E) non-empty experts and every other assignment
+ * packed into whole blocks.
  * Pure host function.  Returns -1 if an argument is negative or block_e < 1. */
 int64_t moe_compact_row_bound(int64_t num_assignments,
                               int32_t num_local_experts, int32_t block_e);

@@ -65,30 +65,31 @@ def test_layout_rule_truth_table(ora):
 
 # ------------------------------------------------------------ compact map
 
-def page_m_indices(counts, starts, block_e, num_rows):
-    """The per-expert padding writer as the page describes it: one program
-    per expert walks its padded rows in steps of block_e and stores e where
-    the row is below the valid count, -1 elsewhere.  Rows past the last
-    region are not written by it (left at -1 here)."""
+def m_indices_by_definition(counts, starts, num_rows):
+    """m_indices from its definition: row r holds e exactly when
+    start_e <= r < start_e + c_e; every other row, padding inside a region
+    and the tail past the last region alike, holds -1 (sglang PR #33128 page,
+    Implementation breakdown item 3 and Key source snippets: padding rows
+    carry expert index -1)."""
+    counts = np.asarray(counts, np.int64)
+    starts = np.asarray(starts, np.int64)
     m = np.full(num_rows, -1, np.int64)
-    for e, (c, st) in enumerate(zip(counts, starts)):
-        padded = -(-c // block_e) * block_e
-        for start_m in range(0, padded, block_e):
-            for i in range(block_e):
-                off = start_m + i
-                m[st + off] = e if off < c else -1
+    labels = np.repeat(np.arange(len(counts)), counts)
+    # position of each real row inside its expert's run
+    first = np.repeat(np.cumsum(counts) - counts, counts)
+    rows = np.repeat(starts, counts) + (np.arange(len(labels)) - first)
+    m[rows] = labels
     return m
 
 
 def psum_starts(counts, align):
     """Region starts by the psum geometry: expert e occupies
-    [align(psum[e-1]), psum[e]) with psum[-1] = 0."""
-    starts, prev_end = [], 0
-    for c in counts:
-        st = -(-prev_end // align) * align
-        starts.append(st)
-        prev_end = st + c
-    return starts, -(-prev_end // align) * align
+    [align(psum[e-1]), psum[e]) with psum[-1] = 0, where psum[e] is the
+    previous region's aligned end plus c_e (a fold over the counts)."""
+    up = lambda n: -(-n // align) * align  # noqa: E731
+    psum = list(itertools.accumulate(counts, lambda end, c: up(end) + c,
+                                     initial=0))
+    return [up(p) for p in psum[:-1]], up(psum[-1])
 
 
 def check_compact_invariants(lay, ids, b, E, block):
@@ -123,12 +124,12 @@ def test_compact_layout_random(ora, seed):
     ids = si.uniform_topk(rng, T, E, K)
     lay = ora.moe_layout(ids, 0, E, "compact", block_e=block)
     check_compact_invariants(lay, ids, 0, E, block)
-    # m_indices equals the page's per-expert padding writer, and the tail
-    # past the last region is padding too
+    # m_indices equals its definition over the psum geometry, the tail past
+    # the last region included
     starts, end = psum_starts(lay["counts"].tolist(), block)
     assert starts == lay["expert_offsets"][:-1].tolist()
     assert end == lay["expert_offsets"][-1]
-    want = page_m_indices(lay["counts"], starts, block, lay["num_rows"])
+    want = m_indices_by_definition(lay["counts"], starts, lay["num_rows"])
     assert np.array_equal(lay["m_indices"], want)
 
 

@@ -1,30 +1,50 @@
 """Pins for the oracle's psum (expanded) layout repack: m_indices from psum,
 expanded -> masked slab, masked slab -> expanded with fused weights.
 
-The fixture follows the masked-slab test the DeepEPv2 page shows
-(`_build_layout`): expert e occupies [align(psum[e-1]), psum[e]), every real
-row holds its own value (s + j) % 200 + 1, doubled on odd columns, so a row
-or column mix-up changes a value."""
+Geometry (DeepEPv2 page, Key source snippets, the layout fixture's
+docstring): expert e occupies rows [align(psum[e-1]), psum[e]) with
+psum[-1] = 0.  The fixture keeps that page's row values (real row r holds
+r mod 200 + 1, twice that on odd columns), so a row or column mix-up
+changes a value; the arrays are built here from the geometry alone."""
+import itertools
+
 import numpy as np
 import pytest
 
 import synthetic_inputs as si
 
 
+def align_up(n, a):
+    return -(-n // a) * a
+
+
+def psum_of(counts, align):
+    """psum by its defining recurrence psum[e] = align(psum[e-1]) + c_e,
+    psum[-1] = 0, as a fold over the counts."""
+    return list(itertools.accumulate(counts, lambda end, c: align_up(end, align)
+                                     + c, initial=0))[1:]
+
+
+def real_rows(counts, starts, n):
+    """Boolean mask of the rows that hold an assignment."""
+    r = np.arange(n)
+    e = np.searchsorted(np.asarray(starts), r, side="right") - 1
+    ok = e >= 0
+    ee = np.where(ok, e, 0)
+    return ok & (r - np.asarray(starts)[ee] < np.asarray(counts)[ee])
+
+
 def build_layout(counts, align, hidden):
-    """The page's fixture geometry and values (float32 rows)."""
-    starts, psum, prev_end = [], [], 0
-    for c in counts:
-        start = -(-prev_end // align) * align
-        starts.append(start)
-        psum.append(start + c)
-        prev_end = start + c
-    total = max(-(-prev_end // align) * align, 1)
-    base = np.zeros((total, hidden), np.float32)
+    """Rows of the expanded layout (float32), psum, region starts and the
+    padded total (at least one row, so an all-empty layout still has a
+    buffer)."""
+    psum = psum_of(counts, align)
+    starts = [align_up(p, align) for p in [0] + psum[:-1]]
+    total = max(align_up(psum[-1], align) if psum else 0, 1)
+    real = real_rows(counts, starts, total)
+    row_val = np.where(real, np.arange(total) % 200 + 1, 0).astype(np.float32)
     gain = 1.0 + (np.arange(hidden) % 2).astype(np.float32)
-    for s, c in zip(starts, counts):
-        for j in range(c):
-            base[s + j] = float((s + j) % 200 + 1) * gain
+    base = row_val[:, None] * gain[None, :]
     return base, np.array(psum, np.int32), starts, total
 
 
@@ -57,9 +77,7 @@ def test_m_indices_tail_masks(ora):
     m = ora.m_indices_from_psum(psum, 128, total + 200)
     for e, (s, c) in enumerate(zip(starts, counts)):
         assert (m[s:s + c] == e).all()
-    real = np.zeros(total + 200, bool)
-    for s, c in zip(starts, counts):
-        real[s:s + c] = True
+    real = real_rows(counts, starts, total + 200)
     assert (m[~real] == -1).all()
     assert starts[:4] == [0, 128, 128, 384]
 
@@ -81,9 +99,7 @@ def test_expand_slab_roundtrip(ora, counts):
     canary = np.full((total, H), 0x7FC0, np.uint16)
     back = ora.masked_slab_to_expand(slab16, mm, psum, align, max_m,
                                      out=canary.copy())
-    real = np.zeros(total, bool)
-    for s, c in zip(starts, counts):
-        real[s:s + c] = True
+    real = real_rows(counts, starts, total)
     assert np.array_equal(back[real], xb[real])
     assert (back[~real] == 0x7FC0).all()
 
@@ -131,9 +147,7 @@ def test_weights_fused_on_real_rows_only(ora):
             assert (np.abs(got - exact) <= 2.0 ** -8 * np.abs(exact)).all()
             # every odd column is twice its even neighbour before rounding
             assert np.allclose(got[1::2], 2 * got[0::2], rtol=2 ** -7)
-    real = np.zeros(total, bool)
-    for s, c in zip(starts, counts):
-        real[s:s + c] = True
+    real = real_rows(counts, starts, total)
     assert (out[~real] == 0x1234).all()
 
 
@@ -146,10 +160,11 @@ def test_scale_copy_by_stride(ora, col_major):
     H, max_m, align, s_cols = 896, 16, 4, 7
     base, psum, starts, total = build_layout(counts, align, H)
     q = np.random.default_rng(1).integers(0, 255, (total, H), np.uint8)
-    sc = np.zeros((total, s_cols), np.float32)
-    for s, c in zip(starts, counts):
-        for j in range(c):
-            sc[s + j] = float((s + j) % 50 + 1) * 0.5 + np.arange(s_cols)
+    # a distinct value per (real row, column); other rows stay 0
+    real = real_rows(counts, starts, total)
+    row_code = np.where(real, (np.arange(total) % 50 + 1) * 0.5, 0.0)
+    sc = np.where(real[:, None], row_code[:, None] + np.arange(s_cols),
+                  0.0).astype(np.float32)
     src = np.ascontiguousarray(sc.T) if col_major else sc
     slab, slab_s, mm, flags = ora.expand_to_masked_slab(
         q, psum, align, max_m, scales=src, scales_col_major=col_major)
