@@ -30,7 +30,7 @@ __all__ = [
     "mxq_abi_version", "moe_m_indices_from_psum", "moe_expand_to_masked_slab",
     "moe_masked_slab_to_expand", "moe_scatter_rows", "upscale_fp8_to_bf16",
     "requant_weight_block_ue8m0", "mxq_mfma_scale_bytes", "mfma_scales",
-    "mxq_copy16", "moe_layout_scatter_quant",
+    "mxq_copy16", "moe_layout_scatter_quant", "moe_layout_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +38,8 @@ LIB_PATH = os.path.join(_HERE, "libmxq.so")
 
 MXQ_OK = 0
 MXQ_ERR_CAPACITY_OVERFLOW = 3
+MXQ_ERR_SCRATCH_LIMIT = 6
+LAYOUT_NOALLOC_SCRATCH_BYTES = 1 << 20
 LAYOUT_KINDS = {"compact": 0, "masked": 1}
 SCALE_FORMATS = {"ue8m0_g128": (0, 128), "e8m0_g32": (1, 32)}
 SCALE_RULES = {"no_clip": 0, "ocp_floor": 1}
@@ -55,6 +57,8 @@ _SIGNATURES = {
     "moe_layout": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                           _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_read_overflow": (_i32, [_p, _p, _p]),
+    "moe_layout_noalloc": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _i64, _p, _p, _p, _p, _p, _p, _p]),
     "moe_scatter_quant": (_i32, [_p, _i64, _i64, _i32, _p, _i32, _i32, _p,
                                  _i64, _p, _i64, _i64, _p]),
     "mx_quant_live_rows": (_i32, [_p, _i64, _i32, _i64, _p, _i32, _i32, _p,
@@ -320,6 +324,34 @@ def moe_layout(topk_ids: torch.Tensor, expert_begin: int,
                           _ptr(lay["overflow_flag"]), _ptr(workspace),
                           workspace.numel(), _stream(ids))
     _check("moe_layout", st)
+    return lay
+
+
+def moe_layout_noalloc(topk_ids: torch.Tensor, expert_begin: int,
+                       num_local_experts: int, kind: str = "compact",
+                       block_e: int = 128, capacity: int = 0,
+                       num_rows: int | None = None, m_indices: bool = True,
+                       out: dict | None = None) -> dict:
+    """``moe_layout`` without a workspace: the library keeps the per-chunk
+    counts in its own static device array (see ``moe_layout_noalloc`` in
+    mxq.h), so with every output given in ``out`` nothing is allocated.
+    Routings that need more than ``LAYOUT_NOALLOC_SCRATCH_BYTES`` of counts
+    raise ``MxqError`` (status ``MXQ_ERR_SCRATCH_LIMIT``).  Calls on one
+    device share that array: overlapping calls race."""
+    ids = _layout_ids(topk_ids)
+    T, K = ids.shape
+    E = num_local_experts
+    k = LAYOUT_KINDS[kind]
+    if num_rows is None:
+        num_rows = (moe_compact_row_bound(T * K, E, block_e) if k == 0
+                    else E * capacity)
+    lay = _layout_outputs(ids, E, num_rows, m_indices, out)
+    st = lib().moe_layout_noalloc(
+        _ptr(ids), T, K, expert_begin, E, k, block_e, capacity, num_rows,
+        _ptr(lay["counts"]), _ptr(lay["expert_offsets"]),
+        _ptr(lay["m_indices"]), _ptr(lay["masked_m"]), _ptr(lay["src2dst"]),
+        _ptr(lay["overflow_flag"]), _stream(ids))
+    _check("moe_layout_noalloc", st)
     return lay
 
 

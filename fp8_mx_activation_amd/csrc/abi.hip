@@ -61,6 +61,8 @@ extern "C" const char* mxq_status_string(mxq_status s) {
       return "workspace missing or too small";
     case MXQ_ERR_HIP:
       return "HIP runtime error";
+    case MXQ_ERR_SCRATCH_LIMIT:
+      return "size exceeds the library's static scratch";
   }
   return "unknown status";
 }

@@ -27,8 +27,17 @@
 //        block_e rows (regions start on multiples of block_e), or a binary
 //        search over the region starts when that table would not fit in the
 //        LDS left over (63 KB per block in all).
+#include <mutex>
+
 #include "layout_device.hpp"
 #include "mxq_host.hpp"
+
+// Per-chunk expert counts of moe_layout_noalloc: a static device array in
+// place of the caller's workspace.  Each device holds its own copy at its
+// own address; host code uses that address (looked up once per device with
+// hipGetSymbolAddress), never this name.
+static __device__ __align__(256) int32_t
+    scratch[MXQ_LAYOUT_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
 
 namespace {
 
@@ -295,14 +304,15 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
 
 }  // namespace
 
-extern "C" mxq_status moe_layout(
-    const int32_t* topk_ids, int64_t T, int32_t K, int32_t expert_begin,
-    int32_t num_local_experts, mxq_layout_kind kind, int32_t block_e,
-    int32_t capacity, int64_t num_rows, int32_t* counts,
-    int32_t* expert_offsets, int32_t* m_indices, int32_t* masked_m,
-    int32_t* src2dst, int32_t* overflow_flag, void* workspace,
-    size_t workspace_bytes, void* stream) {
-  const int32_t E = num_local_experts;
+namespace {
+
+// Host checks of moe_layout's arguments other than the workspace.
+mxq_status layout_args_ok(const int32_t* topk_ids, int64_t T, int32_t K,
+                          int32_t E, mxq_layout_kind kind, int32_t block_e,
+                          int32_t capacity, int64_t num_rows,
+                          const int32_t* counts, const int32_t* expert_offsets,
+                          const int32_t* src2dst,
+                          const int32_t* overflow_flag) {
   if (T < 0 || K < 1 || K > MXQ_MAX_TOPK || E < 1 ||
       E > MXQ_MAX_LOCAL_EXPERTS)
     return MXQ_ERR_INVALID_ARGUMENT;
@@ -323,15 +333,23 @@ extern "C" mxq_status moe_layout(
     return MXQ_ERR_INVALID_ARGUMENT;
   if (A > 0 && (topk_ids == nullptr || src2dst == nullptr))
     return MXQ_ERR_INVALID_ARGUMENT;
-  const LayoutGeom g = layout_geom(A);
-  const size_t need = layout_workspace_bytes(A, E);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return MXQ_ERR_WORKSPACE;
+  return MXQ_OK;
+}
 
+// The launches of moe_layout once its arguments have been checked;
+// chunk_cnt holds at least layout_workspace_bytes(T*K, E) bytes.
+mxq_status layout_launch(const int32_t* topk_ids, int64_t T, int32_t K,
+                         int32_t expert_begin, int32_t E, mxq_layout_kind kind,
+                         int32_t block_e, int32_t capacity, int64_t num_rows,
+                         int32_t* counts, int32_t* expert_offsets,
+                         int32_t* m_indices, int32_t* masked_m,
+                         int32_t* src2dst, int32_t* overflow_flag,
+                         int32_t* chunk_cnt, void* stream) {
+  const int64_t A = T * (int64_t)K;
+  const LayoutGeom g = layout_geom(A);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   hipStream_t s = as_stream(stream);
-  int32_t* chunk_cnt = static_cast<int32_t*>(workspace);
   const int32_t cap = kind == MXQ_LAYOUT_MASKED ? capacity : 0;
   const bool single = A <= kSingleMax;
   if (g.nc > 0 && !single) {
@@ -369,4 +387,80 @@ extern "C" mxq_status moe_layout(
         num_rows, chunk, nc, steps_per_wave, tbl_cap, chunk_cnt, counts,
         expert_offsets, masked_m, overflow_flag, m_indices, src2dst);
   return launch_status();
+}
+
+// Address of this library's scratch array on `dev`, looked up once per
+// device with that device current (each device has its own copy).
+mxq_status scratch_on_device(int dev, int32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return MXQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return MXQ_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return MXQ_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return MXQ_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return MXQ_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = static_cast<int32_t*>(addr[dev]);
+  return MXQ_OK;
+}
+
+}  // namespace
+
+extern "C" mxq_status moe_layout(
+    const int32_t* topk_ids, int64_t T, int32_t K, int32_t expert_begin,
+    int32_t num_local_experts, mxq_layout_kind kind, int32_t block_e,
+    int32_t capacity, int64_t num_rows, int32_t* counts,
+    int32_t* expert_offsets, int32_t* m_indices, int32_t* masked_m,
+    int32_t* src2dst, int32_t* overflow_flag, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const int32_t E = num_local_experts;
+  const mxq_status st =
+      layout_args_ok(topk_ids, T, K, E, kind, block_e, capacity, num_rows,
+                     counts, expert_offsets, src2dst, overflow_flag);
+  if (st != MXQ_OK) return st;
+  const size_t need = layout_workspace_bytes(T * (int64_t)K, E);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return MXQ_ERR_WORKSPACE;
+  return layout_launch(topk_ids, T, K, expert_begin, E, kind, block_e,
+                       capacity, num_rows, counts, expert_offsets, m_indices,
+                       masked_m, src2dst, overflow_flag,
+                       static_cast<int32_t*>(workspace), stream);
+}
+
+extern "C" mxq_status moe_layout_noalloc(
+    const int32_t* topk_ids, int64_t T, int32_t K, int32_t expert_begin,
+    int32_t num_local_experts, mxq_layout_kind kind, int32_t block_e,
+    int32_t capacity, int64_t num_rows, int32_t* counts,
+    int32_t* expert_offsets, int32_t* m_indices, int32_t* masked_m,
+    int32_t* src2dst, int32_t* overflow_flag, void* stream) {
+  const int32_t E = num_local_experts;
+  const mxq_status st =
+      layout_args_ok(topk_ids, T, K, E, kind, block_e, capacity, num_rows,
+                     counts, expert_offsets, src2dst, overflow_flag);
+  if (st != MXQ_OK) return st;
+  const size_t need = layout_workspace_bytes(T * (int64_t)K, E);
+  if (need > MXQ_LAYOUT_NOALLOC_SCRATCH_BYTES) return MXQ_ERR_SCRATCH_LIMIT;
+  int32_t* chunk_cnt = nullptr;
+  if (need > 0) {
+    // the stream's device (the current one for the null stream)
+    int dev = -1;
+    hipStream_t s = as_stream(stream);
+    if (s == nullptr) {
+      if (hipGetDevice(&dev) != hipSuccess) return MXQ_ERR_HIP;
+    } else if (hipStreamGetDevice(s, &dev) != hipSuccess) {
+      return MXQ_ERR_HIP;
+    }
+    const mxq_status ss = scratch_on_device(dev, &chunk_cnt);
+    if (ss != MXQ_OK) return ss;
+  }
+  return layout_launch(topk_ids, T, K, expert_begin, E, kind, block_e,
+                       capacity, num_rows, counts, expert_offsets, m_indices,
+                       masked_m, src2dst, overflow_flag, chunk_cnt, stream);
 }

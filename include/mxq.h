@@ -54,6 +54,8 @@ extern "C" {
 #define MXQ_MAX_TOPK 64
 #define MXQ_MAX_ASSIGNMENTS (1 << 24) /* T*K limit of moe_layout */
 #define MXQ_MAX_HIDDEN 32768 /* moe_scatter_quant stages one row in LDS */
+/* Static device scratch of moe_layout_noalloc, per device (1 MiB). */
+#define MXQ_LAYOUT_NOALLOC_SCRATCH_BYTES (1u << 20)
 
 typedef enum {
   MXQ_OK = 0,
@@ -61,7 +63,8 @@ typedef enum {
   MXQ_ERR_UNSUPPORTED = 2,
   MXQ_ERR_CAPACITY_OVERFLOW = 3,
   MXQ_ERR_WORKSPACE = 4,
-  MXQ_ERR_HIP = 5
+  MXQ_ERR_HIP = 5,
+  MXQ_ERR_SCRATCH_LIMIT = 6 /* beyond the library's static scratch */
 } mxq_status;
 
 typedef enum { MXQ_LAYOUT_COMPACT = 0, MXQ_LAYOUT_MASKED = 1 } mxq_layout_kind;
@@ -154,6 +157,30 @@ mxq_status moe_layout(const int32_t* topk_ids, int64_t T, int32_t K,
  * it is set, MXQ_OK otherwise [P3 Review highlights: overflow fails fast]. */
 mxq_status moe_read_overflow(const int32_t* overflow_flag, int32_t* host_value,
                              void* stream);
+
+/* moe_layout without a workspace argument, for callers that cannot allocate
+ * device memory (code under hipGraph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, outputs and results are those of
+ * moe_layout; the per-chunk counts that moe_layout keeps in the caller's
+ * workspace live instead in a static device array of the library,
+ * MXQ_LAYOUT_NOALLOC_SCRATCH_BYTES per device, held until the process ends.
+ * A routing whose moe_layout_workspace_bytes(T, K, E) exceeds that returns
+ * MXQ_ERR_SCRATCH_LIMIT and enqueues nothing (the prefill routing of 8192
+ * tokens, top-8 over 256 experts needs 64 KiB; none is needed when
+ * T*K <= 4096).  The call allocates nothing.  Its first call on a device
+ * looks up that device's copy of the array (a host query, no allocation);
+ * make it outside graph capture.  Every call on one device shares the array:
+ * calls that overlap on one device (e.g. on two streams) race and must be
+ * ordered by the caller.  The array needs no clearing: each call overwrites
+ * what it reads.  The stream's device is the one used. */
+mxq_status moe_layout_noalloc(const int32_t* topk_ids, int64_t T, int32_t K,
+                              int32_t expert_begin, int32_t num_local_experts,
+                              mxq_layout_kind kind, int32_t block_e,
+                              int32_t capacity, int64_t num_rows,
+                              int32_t* counts, int32_t* expert_offsets,
+                              int32_t* m_indices, int32_t* masked_m,
+                              int32_t* src2dst, int32_t* overflow_flag,
+                              void* stream);
 
 /* ---------------------------------------------------------- scatter + quant */
 

@@ -282,6 +282,34 @@ def test_layout_validation(mxq):
     assert call(T=(1 << 21) + 1, K=8, rows=1 << 30) == UNSUPPORTED  # > 2^24
 
 
+def test_layout_noalloc_validation(mxq):
+    """The allocation-free layout checks what moe_layout checks and refuses
+    a routing whose per-chunk counts exceed its static scratch, all before
+    any HIP call."""
+    L = mxq.lib()
+    SCRATCH = 6
+
+    def call(T=8, K=2, E=4, kind=0, block=128, cap=0, rows=None, ids=FAKE):
+        if rows is None:
+            rows = mxq.moe_compact_row_bound(T * K, E, block)
+        return L.moe_layout_noalloc(ids, T, K, 0, E, kind, block, cap, rows,
+                                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+
+    assert call(rows=100) == INVALID
+    assert call(E=0) == INVALID
+    assert call(kind=5) == UNSUPPORTED
+    assert call(ids=None) == INVALID
+    assert call(T=(1 << 21) + 1, K=8, rows=1 << 30) == UNSUPPORTED
+    # 2^24 assignments over 1024 experts: 2048 chunks x 1024 counts = 8 MiB
+    assert mxq.moe_layout_workspace_bytes(1 << 21, 8, 1024) == 8 << 20
+    assert call(T=1 << 21, K=8, E=1024) == SCRATCH
+    assert mxq.MXQ_ERR_SCRATCH_LIMIT == SCRATCH
+    assert b"scratch" in L.mxq_status_string(SCRATCH)
+    # the prefill routing (8192 x top-8 over 256 experts) fits: 64 KiB
+    assert mxq.moe_layout_workspace_bytes(8192, 8, 256) <= \
+        mxq.LAYOUT_NOALLOC_SCRATCH_BYTES
+
+
 def test_combine_requant_live_validation(mxq):
     L = mxq.lib()
     assert L.moe_combine(FAKE, 256, 16, FAKE, FAKE, 4, 2, 260, FAKE, 260, 0,
