@@ -4,18 +4,20 @@
 // breakdown items 1-2).
 //
 // Two launches with static grids:
-//   requant_amax_kernel   block b owns a contiguous run of rows.  No e4m3
-//                         magnitude exceeds 448, so row t's value
-//                         fl(dec(max|q_t|) * s_t) is at most
+//   requant_amax_kernel   one wavefront per block, owning a contiguous run of
+//                         rows.  No e4m3 magnitude exceeds 448, so row t's
+//                         value fl(dec(max|q_t|) * s_t) is at most
 //                         bound_t = fl(448 * s_t) (rounding is monotone).
-//                         The block reads the scales of its rows, then reads
-//                         in full only the rows that can still raise its
-//                         maximum: first those whose bound is the largest,
-//                         then those whose bound exceeds what the first ones
-//                         gave.  Every skipped row has bound_t <= the block's
-//                         maximum, so the maximum is exact.  When the token
-//                         scales differ, most rows are never read; with equal
-//                         scales every row is.  Each block writes its maximum
+//                         The wavefront reads the scales of its rows, then
+//                         reads rows in full in descending order of bound
+//                         (four at a time) until no row left has a bound above
+//                         the maximum found.  Every skipped row has
+//                         bound_t <= that maximum, so the maximum is exact.
+//                         A row holding +-448 (what a per-token absmax
+//                         quantizer produces) attains its bound, so one row
+//                         read settles a run; rows below their bounds are read
+//                         until the bounds fall under the maximum, every row
+//                         in the worst case.  Each block writes its maximum
 //                         (fp32 bits of a non-negative float order like
 //                         unsigned integers) to workspace.
 //   requant_apply_kernel  every block reduces the partials (a few KB from
@@ -55,114 +57,97 @@ __device__ __forceinline__ uint32_t requant4(uint32_t w, float st, float inv) {
                     (hi[0] * st) * inv, (hi[1] * st) * inv);
 }
 
+// Rows of the max pass read together by one wavefront.
 constexpr int kRowsPerWave = 4;
 
-// Rows a block of the max pass owns at least, and how many of them it ranks
-// at once (four per thread).
+// Rows a block of the max pass owns at least.
 constexpr int64_t kAmaxMinRows = 16;
-constexpr int kAmaxChunk = 1024;
 
-// Max over the block of a value every thread holds; red is 4 words of LDS.
-// Ends with a barrier, so red (and any LDS read before the call) may be
-// reused right after it.
-__device__ __forceinline__ uint32_t block_max4(uint32_t v, uint32_t* red) {
+// Largest fl(dec(max|q_r|) * s_r), as fp32 bits, over the rows row[0..NR)
+// (NR = 1 or kRowsPerWave; s_r from lane r_lane[u] of `s`).  Every lane
+// takes 16-byte columns lane*16, lane*16 + 1024, ... of each row, so the
+// NR rows' loads of four column steps are in flight together.
+template <int NR>
+__device__ __forceinline__ uint32_t rows_value_max(
+    const uint8_t* __restrict__ q, int64_t ld, int32_t H, const int64_t* row,
+    const int* r_lane, float s) {
   const int lane = threadIdx.x & 63;
-  v = wave_max(v);
-  if (lane == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
-  __syncthreads();
-  return m;
-}
-
-// fl(dec(max|q_t|) * s_t) as fp32 bits, max over the listed rows that each
-// wavefront takes (entries wv, wv + 4, wv + 8, wv + 12, then the next 16),
-// so a lane keeps up to 16 loads of four different rows in flight.
-__device__ __forceinline__ uint32_t listed_rows_max(
-    const uint8_t* __restrict__ q, int64_t ld, const float* __restrict__ sc,
-    int32_t H, int64_t row0, const int32_t* list, int n) {
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
   const int64_t H16 = (int64_t)(H / 16) * 16;
-  uint32_t best = 0;
-  for (int e0 = wv; e0 < n; e0 += 4 * kRowsPerWave) {
-    int64_t row[kRowsPerWave];
-    bool ok[kRowsPerWave];
+  uint32_t m[NR];
 #pragma unroll
-    for (int u = 0; u < kRowsPerWave; ++u) {
-      const int e = e0 + 4 * u;
-      ok[u] = e < n;
-      row[u] = row0 + list[ok[u] ? e : e0];
-    }
-    uint32_t m[kRowsPerWave] = {0, 0, 0, 0};
+  for (int u = 0; u < NR; ++u) m[u] = 0;
 #pragma unroll 4
-    for (int64_t col = lane * 16; col < H16; col += 64 * 16) {
-      u32x4 v[kRowsPerWave];
+  for (int64_t col = lane * 16; col < H16; col += 64 * 16) {
+    u32x4 v[NR];
 #pragma unroll
-      for (int u = 0; u < kRowsPerWave; ++u)
-        v[u] = ok[u] ? load16(q + row[u] * ld + col) : u32x4{0, 0, 0, 0};
+    for (int u = 0; u < NR; ++u) v[u] = load16(q + row[u] * ld + col);
 #pragma unroll
-      for (int u = 0; u < kRowsPerWave; ++u) m[u] = max(m[u], mag_max16(v[u]));
-    }
+    for (int u = 0; u < NR; ++u) m[u] = max(m[u], mag_max16(v[u]));
+  }
+  uint32_t best = 0;
 #pragma unroll
-    for (int u = 0; u < kRowsPerWave; ++u) {
-      if (!ok[u]) break;
-      const uint8_t* r = q + row[u] * ld;
-      for (int64_t col = H16 + lane; col < H; col += 64)
-        m[u] = max(m[u], (uint32_t)(r[col] & 0x7F));
-      const uint32_t mm = wave_max(m[u]);
-      const float rq = __builtin_amdgcn_cvt_f32_fp8((int)mm, 0) * sc[row[u]];
-      best = max(best, __float_as_uint(rq));
-    }
+  for (int u = 0; u < NR; ++u) {
+    const uint8_t* r = q + row[u] * ld;
+    for (int64_t col = H16 + lane; col < H; col += 64)
+      m[u] = max(m[u], (uint32_t)(r[col] & 0x7F));
+    const uint32_t mm = wave_max(m[u]);
+    const float su = __int_as_float(
+        __builtin_amdgcn_readlane(__float_as_int(s), r_lane[u]));
+    const float rq = __builtin_amdgcn_cvt_f32_fp8((int)mm, 0) * su;
+    best = max(best, __float_as_uint(rq));
   }
   return best;
 }
 
-__global__ __launch_bounds__(256) void requant_amax_kernel(
+// One wavefront per block, owning rows [b * rows_per_block, ...).  For each
+// run of 64 rows, lane i holds row i's scale and bound fl(448 * s).  Rows
+// are then read in descending order of their bound, up to four at a time,
+// until no row left has a bound above the maximum found: a row with
+// bound <= that maximum cannot raise it.  Rows produced by a per-token
+// absmax quantizer hold +-448, so their value equals their bound and the
+// first row read settles its run.
+__global__ __launch_bounds__(64) void requant_amax_kernel(
     const uint8_t* __restrict__ q, int64_t ld, const float* __restrict__ sc,
     int64_t T, int32_t H, int64_t rows_per_block,
     uint32_t* __restrict__ partial) {
-  __shared__ int32_t list[kAmaxChunk];
-  __shared__ uint32_t red[4];
-  __shared__ int32_t nlist;
+  const int lane = threadIdx.x;
   const int64_t r_begin = (int64_t)blockIdx.x * rows_per_block;
   const int64_t r_end = min(T, r_begin + rows_per_block);
-  uint32_t L = 0;  // the block's maximum so far, block-uniform
-  for (int64_t c0 = r_begin; c0 < r_end; c0 += kAmaxChunk) {
-    const int n = (int)min((int64_t)kAmaxChunk, r_end - c0);
-    uint32_t bnd[4];
-    uint32_t bmax = 0;
-    // the four scales are loaded unconditionally (index clamped to the
-    // run's last row) so that they are in flight together
-    float sv[4];
+  uint32_t L = 0;  // the block's maximum so far (wave-uniform)
+  for (int64_t c0 = r_begin; c0 < r_end; c0 += 64) {
+    const int n = (int)min((int64_t)64, r_end - c0);
+    // index clamped to the run's last row, so the load is unconditional
+    const float s = sc[c0 + min(lane, n - 1)];
+    const uint32_t bnd = lane < n ? __float_as_uint(448.0f * s) : 0u;
+    uint64_t cand = __ballot(bnd > L);
+    while (cand != 0) {
+      const uint32_t Bc = __builtin_amdgcn_readfirstlane(
+          wave_max(((cand >> lane) & 1) ? bnd : 0u));
+      if (Bc <= L) break;
+      uint64_t top = cand & __ballot(bnd == Bc);
+      int64_t row[kRowsPerWave];
+      int r_lane[kRowsPerWave] = {};
+      int nr = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      sv[u] = sc[c0 + min((int)threadIdx.x + 256 * u, n - 1)];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = threadIdx.x + 256 * u;
-      bnd[u] = i < n ? __float_as_uint(448.0f * sv[u]) : 0u;
-      bmax = max(bmax, bnd[u]);
-    }
-    const uint32_t B = block_max4(bmax, red);
-    if (B <= L) continue;  // no row of this run can raise the maximum
-    // First the rows whose bound is the largest, then those whose bound lies
-    // strictly between the maximum they give and that largest bound.
-    for (int phase = 0; phase < 2; ++phase) {
-      if (threadIdx.x == 0) nlist = 0;
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool take = phase == 0 ? bnd[u] == B : (bnd[u] > L && bnd[u] < B);
-        if (take) list[atomicAdd(&nlist, 1)] = threadIdx.x + 256 * u;
+      for (int u = 0; u < kRowsPerWave; ++u) {
+        const int i = top ? __builtin_ctzll(top) : r_lane[0];
+        if (top) {
+          top &= top - 1;
+          cand &= ~(1ull << i);
+          ++nr;
+        }
+        r_lane[u] = i;  // past the last taken row: repeats the first
+        row[u] = c0 + i;
       }
-      __syncthreads();
-      const int nl = nlist;
-      if (nl == 0) break;  // block-uniform
-      L = max(L, block_max4(listed_rows_max(q, ld, sc, H, c0, list, nl), red));
+      const uint32_t v = nr == 1
+                             ? rows_value_max<1>(q, ld, H, row, r_lane, s)
+                             : rows_value_max<kRowsPerWave>(q, ld, H, row,
+                                                            r_lane, s);
+      L = max(L, v);
+      cand &= __ballot(bnd > L);
     }
   }
-  if (threadIdx.x == 0) partial[blockIdx.x] = L;
+  if (lane == 0) partial[blockIdx.x] = L;
 }
 
 // A wavefront takes one row at a time (rows w, w + S, ... with S = number
@@ -171,9 +156,21 @@ __global__ __launch_bounds__(256) void requant_amax_kernel(
 // interleaves reads and streaming writes finely; with four rows per
 // wavefront in flight instead, the pass took 30.7 us rather than 24.6 us at
 // 16384 x 4096 with its input in HBM (the same 22.5 us from the MALL).
+// The first chunk's loads (and its row's scale) are issued before the
+// partial maxima are reduced, so that reduction waits behind them.
 // q_in and q_out may be the same buffer: every byte is read and then written
 // by the same lane.
 constexpr int kApplyBatch = 4;
+
+__device__ __forceinline__ void load_batch(const uint8_t* src, int64_t c0,
+                                           int64_t H16,
+                                           u32x4 (&v)[kApplyBatch]) {
+#pragma unroll
+  for (int b = 0; b < kApplyBatch; ++b) {
+    const int64_t col = c0 + b * 64 * 16;
+    v[b] = col < H16 ? load16(src + col) : u32x4{0, 0, 0, 0};
+  }
+}
 
 __global__ __launch_bounds__(256) void requant_apply_kernel(
     const uint8_t* q_in, int64_t ld_in, const float* __restrict__ sc,
@@ -183,6 +180,17 @@ __global__ __launch_bounds__(256) void requant_apply_kernel(
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   __shared__ uint32_t red[4];
+  const int64_t H16 = (int64_t)(H / 16) * 16;
+  const int64_t S = (int64_t)gridDim.x * 4;
+  int64_t row = (int64_t)blockIdx.x * 4 + wv;
+  // first chunk of this wavefront's first row, in flight during the
+  // reduction below
+  u32x4 v[kApplyBatch];
+  float st = 0.0f;
+  if (row < T) {
+    st = sc[row];
+    load_batch(q_in + row * ld_in, lane * 16, H16, v);
+  }
   // the partials four per thread and round, loaded unconditionally (index
   // clamped to the last one; a repeated partial leaves the maximum as it
   // is) so that they are in flight together
@@ -203,19 +211,14 @@ __global__ __launch_bounds__(256) void requant_apply_kernel(
   const float inv = 1.0f / S_t;
   if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = S_t;
 
-  const int64_t H16 = (int64_t)(H / 16) * 16;
-  const int64_t S = (int64_t)gridDim.x * 4;
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wv; row < T; row += S) {
-    const float st = sc[row];
+  bool loaded = true;  // v holds the first chunk of `row`
+  for (; row < T; row += S) {
+    if (!loaded) st = sc[row];
     const uint8_t* src = q_in + row * ld_in;
     uint8_t* dst = q_out + row * ld_out;
     for (int64_t c0 = lane * 16; c0 < H16; c0 += kApplyBatch * 64 * 16) {
-      u32x4 v[kApplyBatch];
-#pragma unroll
-      for (int b = 0; b < kApplyBatch; ++b) {
-        const int64_t col = c0 + b * 64 * 16;
-        v[b] = col < H16 ? load16(src + col) : u32x4{0, 0, 0, 0};
-      }
+      if (!loaded) load_batch(src, c0, H16, v);
+      loaded = false;
 #pragma unroll
       for (int b = 0; b < kApplyBatch; ++b) {
         const int64_t col = c0 + b * 64 * 16;
@@ -228,6 +231,7 @@ __global__ __launch_bounds__(256) void requant_apply_kernel(
         store16_nt(dst + col, o);
       }
     }
+    loaded = false;
     for (int64_t col = H16 + lane; col < H; col += 64)
       dst[col] = (uint8_t)requant4(src[col], st, inv);
   }
@@ -266,7 +270,7 @@ extern "C" mxq_status requant_per_token_to_per_tensor(
   if (rows_per_block < kAmaxMinRows) rows_per_block = kAmaxMinRows;
   const int64_t np = ceil_div(T, rows_per_block);
   if (np > 0) {
-    requant_amax_kernel<<<(unsigned)np, 256, 0, s>>>(
+    requant_amax_kernel<<<(unsigned)np, 64, 0, s>>>(
         static_cast<const uint8_t*>(q_in_fp8), ld_in, token_scales, T, H,
         rows_per_block, partial);
     if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;

@@ -99,8 +99,8 @@ def test_requant_non_power_of_two_scales(ora):
 
 
 def test_requant_more_rows_than_one_ranking_round(ora):
-    """T = 1.1M rows: each block of the max pass owns 1075 rows and ranks
-    them in two runs of at most 1024, carrying its maximum across."""
+    """T = 1.1M rows: each block of the max pass owns 1075 rows and screens
+    them in runs of 64, carrying its maximum across runs."""
     rng = np.random.default_rng(13)
     T, H = 1_100_000, 16
     u = rng.integers(-6, 3, size=T)
@@ -108,6 +108,23 @@ def test_requant_more_rows_than_one_ranking_round(ora):
     amax = np.exp2(rng.uniform(0.0, np.log2(448.0), size=T))
     q = fp8_rows_with_amax(rng, amax, H)
     requant_both(ora, q, s)
+
+
+def test_requant_equal_bounds_below_448(ora):
+    """Equal token scales and no row holding 448: every row's bound equals
+    the largest, no row attains it, so the max pass reads every row, four
+    at a time, and the maximum may sit in any of them.  Then the same rows
+    with one row per 64 reaching 448 at a random place."""
+    rng = np.random.default_rng(14)
+    for T, H in ((1000, 64), (4099, 4096), (130, 112)):
+        s = np.full(T, 2.0 ** -3, np.float32)
+        amax = rng.uniform(1.0, 400.0, size=T)
+        q = fp8_rows_with_amax(rng, amax, H)
+        requant_both(ora, q, s)
+        for r0 in range(0, T, 64):
+            amax[r0 + int(rng.integers(0, min(64, T - r0)))] = 448.0
+        q = fp8_rows_with_amax(rng, amax, H)
+        requant_both(ora, q, s)
 
 
 def test_requant_operation_order_cases(ora):
