@@ -15,9 +15,10 @@
 //   moe_scatter_rows           the prefill path: a dispatcher's quantized
 //                              rows and scales written into the contiguous
 //                              layout (psum offsets) by src2dst.
-// The copies launch blocks per (expert, range of slab rows); a block deals
-// its rows' 16-byte vectors to its threads and issues a round of loads
-// before the stores.  All grids depend only on host arguments, so every call
+// The copies of large slabs launch blocks per (expert, range of slab rows);
+// a block deals its rows' 16-byte vectors to its threads and issues a round
+// of loads before the stores.  Small slabs with at most 64 experts use a
+// fixed grid that deals (real row, chunk) units to wavefronts instead.  All grids depend only on host arguments, so every call
 // can be captured in a hipGraph.
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
@@ -95,6 +96,27 @@ inline CopyShape copy_shape(int32_t E, int32_t max_m, int64_t vec_per_row) {
   if (rpb < floor_rows) rpb = floor_rows;
   if (rpb < 1) rpb = 1;
   return {rpb, threads};
+}
+
+// Small slabs (at most 4M 16-byte vectors) with at most 64 experts take the
+// unit kernels below, whose grid holds at most kSmallBlocks blocks, fewer
+// when the slab holds fewer units.
+constexpr int kUnitVec = 256;  // 16-byte vectors per unit of work
+constexpr int kUnitPerLane = kUnitVec / 64;
+constexpr int kSmallBlocks = 256;
+constexpr int kSmallThreads = 256;
+constexpr int kSmallExperts = 64;  // one per lane of a wavefront
+
+inline bool use_small_copy(int32_t E, int32_t max_m, int64_t vec_per_row) {
+  const int64_t v = vec_per_row > 0 ? vec_per_row : 1;
+  return E <= kSmallExperts && (int64_t)E * max_m * v <= ((int64_t)4 << 20);
+}
+
+inline unsigned small_blocks(int32_t E, int32_t max_m, int64_t vec_per_row) {
+  const int64_t upr = vec_per_row > 0 ? ceil_div(vec_per_row, kUnitVec) : 1;
+  int64_t b = ceil_div((int64_t)E * max_m * upr, kSmallThreads / 64);
+  if (b > kSmallBlocks) b = kSmallBlocks;
+  return (unsigned)(b < 1 ? 1 : b);
 }
 
 // Block (e, b) copies rows [b*rpb, (b+1)*rpb) of expert e's slab, limited to
@@ -236,6 +258,180 @@ __global__ __launch_bounds__(kCopyThreads) void slab_to_expand_kernel(
   }
 }
 
+// Small slabs with at most 64 experts: a fixed grid that does not grow with
+// E * max_m.  Lane e of every wavefront holds expert e's row range
+// (start_e, clipped count c_e) and the inclusive prefix of the counts, so
+// real row i (in expert order) belongs to expert e = #{prefix <= i}, one
+// ballot.  Work comes in units of (real row, chunk of kUnitVec 16-byte
+// vectors); unit u goes to wavefront u mod W of the W in the grid, numbered
+// across blocks first so that consecutive units land on different CUs.  A
+// wavefront issues the kUnitVec / 64 loads of a unit before its stores.
+
+struct LaneRange {
+  int64_t start;  // first source (expanded) row of expert `lane`
+  int c;          // clipped row count of expert `lane` (0 past E)
+  int incl;       // inclusive prefix of c over experts <= lane
+};
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Expert and position of real row i: returns e and sets j (row within e).
+__device__ __forceinline__ int row_owner(const LaneRange& r, int E, int i,
+                                         int& j) {
+  const int lane = threadIdx.x & 63;
+  const int e = __popcll(__ballot(lane < E && r.incl <= i));
+  j = i - (__builtin_amdgcn_readlane(r.incl, e) -
+           __builtin_amdgcn_readlane(r.c, e));
+  return e;
+}
+
+__global__ __launch_bounds__(kSmallThreads) void expand_to_slab_small_kernel(
+    const uint8_t* __restrict__ x, int64_t ld_x, int64_t src_rows,
+    int64_t row_bytes, const uint8_t* __restrict__ xs, int64_t xs_rs,
+    int64_t xs_cs, int32_t s_cols, int32_t s_elem,
+    const int32_t* __restrict__ psum, int32_t E, int32_t align, int32_t max_m,
+    uint8_t* __restrict__ slab, int64_t ld_slab, uint8_t* __restrict__ ss,
+    int64_t ss_rs, int64_t ss_cs, int32_t* __restrict__ masked_m,
+    int32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int el = min(lane, E - 1);
+  const int64_t p_cur = psum[el];
+  const int64_t p_prev = el == 0 ? 0 : (int64_t)psum[el - 1];
+  const int64_t pp = p_prev < 0 ? 0 : p_prev;
+  LaneRange r;
+  r.start = (pp + align - 1) / align * align;
+  int64_t c = p_cur - r.start;
+  c = c > 0 ? c : 0;
+  int f = 0;
+  if (c > max_m) { f |= 1; c = max_m; }
+  if (r.start + c > src_rows) {
+    f |= 2;
+    c = src_rows > r.start ? src_rows - r.start : 0;
+  }
+  if (lane >= E) { c = 0; f = 0; }
+  r.c = (int)c;
+  r.incl = wave_incl_scan(r.c);
+  if (blockIdx.x == 0 && threadIdx.x < 64) {  // one writer of the outputs
+    if (lane < E) masked_m[lane] = r.c;
+    const bool any1 = __ballot(f & 1) != 0, any2 = __ballot(f & 2) != 0;
+    if (lane == 0) *flags = (any1 ? 1 : 0) | (any2 ? 2 : 0);
+  }
+  const int total = __builtin_amdgcn_readlane(r.incl, 63);
+  const int nvec = (int)(row_bytes / 16);
+  // at least one unit per row: the first unit of a row also copies its
+  // scales (rows of zero bytes still have them)
+  const int upr = nvec > 0 ? (nvec + kUnitVec - 1) / kUnitVec : 1;
+  const int64_t units = (int64_t)total * upr;
+  const int64_t W = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t gw = (int64_t)(threadIdx.x >> 6) * gridDim.x + blockIdx.x;
+  for (int64_t u = gw; u < units; u += W) {
+    const int i = (int)(u / upr);
+    const int k = (int)(u - (int64_t)i * upr);
+    int j;
+    const int e = row_owner(r, E, i, j);
+    const int64_t st = ((int64_t)__builtin_amdgcn_readlane(
+                            (int)(r.start >> 32), e) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)r.start, e);
+    const int64_t src_row = st + j;
+    const int64_t dst_row = (int64_t)e * max_m + j;
+    const uint8_t* src = x + src_row * ld_x;
+    uint8_t* dst = slab + dst_row * ld_slab;
+    if (nvec > 0) {
+      u32x4 v[kUnitPerLane];
+#pragma unroll
+      for (int w = 0; w < kUnitPerLane; ++w) {
+        const int vi = k * kUnitVec + w * 64 + lane;
+        // index clamped to the row's last vector: every load is issued
+        v[w] = load16(src + (int64_t)min(vi, nvec - 1) * 16);
+      }
+#pragma unroll
+      for (int w = 0; w < kUnitPerLane; ++w) {
+        const int vi = k * kUnitVec + w * 64 + lane;
+        if (vi < nvec) store16(dst + (int64_t)vi * 16, v[w]);
+      }
+    }
+    if (k == 0 && xs != nullptr) {
+      for (int g = lane; g < s_cols; g += 64) {
+        const uint8_t* sp = xs + src_row * xs_rs + g * xs_cs;
+        uint8_t* dp = ss + dst_row * ss_rs + g * ss_cs;
+        if (s_elem == 4) {
+          uint32_t w;
+          __builtin_memcpy(&w, sp, 4);
+          __builtin_memcpy(dp, &w, 4);
+        } else {
+          *dp = *sp;
+        }
+      }
+    }
+  }
+}
+
+template <bool WEIGHTED>
+__global__ __launch_bounds__(kSmallThreads) void slab_to_expand_small_kernel(
+    const uint16_t* __restrict__ slab, int64_t ld_slab, int32_t H,
+    const int32_t* __restrict__ masked_m, const int32_t* __restrict__ psum,
+    int32_t E, int32_t align, int32_t max_m, const float* __restrict__ wts,
+    uint16_t* __restrict__ out, int64_t ld_out, int64_t out_rows) {
+  const int lane = threadIdx.x & 63;
+  const int el = min(lane, E - 1);
+  const int64_t p_prev = el == 0 ? 0 : (int64_t)psum[el - 1];
+  int64_t c = masked_m[el];
+  const int64_t pp = p_prev < 0 ? 0 : p_prev;
+  LaneRange r;
+  r.start = (pp + align - 1) / align * align;
+  if (c > max_m) c = max_m;
+  if (r.start + c > out_rows) c = out_rows > r.start ? out_rows - r.start : 0;
+  if (c < 0 || lane >= E) c = 0;
+  r.c = (int)c;
+  r.incl = wave_incl_scan(r.c);
+  const int total = __builtin_amdgcn_readlane(r.incl, 63);
+  const int nvec = H / 8;
+  const int upr = (nvec + kUnitVec - 1) / kUnitVec;
+  const int64_t units = (int64_t)total * upr;
+  const int64_t W = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t gw = (int64_t)(threadIdx.x >> 6) * gridDim.x + blockIdx.x;
+  for (int64_t u = gw; u < units; u += W) {
+    const int i = (int)(u / upr);
+    const int k = (int)(u - (int64_t)i * upr);
+    int j;
+    const int e = row_owner(r, E, i, j);
+    const int64_t st = ((int64_t)__builtin_amdgcn_readlane(
+                            (int)(r.start >> 32), e) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)r.start, e);
+    const int64_t orow = st + j;
+    const uint16_t* src = slab + ((int64_t)e * max_m + j) * ld_slab;
+    uint16_t* dst = out + orow * ld_out;
+    const float wv = WEIGHTED ? wts[orow] : 1.0f;
+    u32x4 v[kUnitPerLane];
+#pragma unroll
+    for (int w = 0; w < kUnitPerLane; ++w) {
+      const int vi = k * kUnitVec + w * 64 + lane;
+      v[w] = load16(src + (int64_t)min(vi, nvec - 1) * 8);
+    }
+#pragma unroll
+    for (int w = 0; w < kUnitPerLane; ++w) {
+      const int vi = k * kUnitVec + w * 64 + lane;
+      if (vi >= nvec) continue;
+      u32x4 o = v[w];
+      if (WEIGHTED) {
+        o.x = scale_bf16x2(o.x, wv);
+        o.y = scale_bf16x2(o.y, wv);
+        o.z = scale_bf16x2(o.z, wv);
+        o.w = scale_bf16x2(o.w, wv);
+      }
+      store16(dst + (int64_t)vi * 8, o);
+    }
+  }
+}
+
 // One block per token: each thread loads its 16-byte vectors of the row once
 // and stores them to every destination of the token (streaming stores);
 // scale entries are copied through their strides.
@@ -360,6 +556,17 @@ extern "C" mxq_status moe_expand_to_masked_slab(
          (xs_row_stride | xs_col_stride | ss_row_stride | ss_col_stride) % 4))
       return MXQ_ERR_INVALID_ARGUMENT;
   }
+  if (use_small_copy(E, max_m, row_bytes / 16)) {
+    expand_to_slab_small_kernel<<<small_blocks(E, max_m, row_bytes / 16),
+                                  kSmallThreads, 0, as_stream(stream)>>>(
+        static_cast<const uint8_t*>(x), ld_x, src_rows, row_bytes,
+        static_cast<const uint8_t*>(x_scales), xs_row_stride, xs_col_stride,
+        scale_cols, scale_elem_bytes, psum, E, align, max_m,
+        static_cast<uint8_t*>(slab), ld_slab,
+        static_cast<uint8_t*>(slab_scales), ss_row_stride, ss_col_stride,
+        masked_m, flags);
+    return launch_status();
+  }
   const CopyShape cs = copy_shape(E, max_m, row_bytes / 16);
   const int64_t rpb = cs.rows_per_block;
   const int64_t blocks = (int64_t)E * ceil_div(max_m, rpb);
@@ -391,13 +598,27 @@ extern "C" mxq_status moe_masked_slab_to_expand(
   if (!aligned16(slab_bf16) || (ld_slab * 2) % 16 != 0 || ld_slab < H ||
       !aligned16(out_bf16) || (ld_out * 2) % 16 != 0 || ld_out < H)
     return MXQ_ERR_INVALID_ARGUMENT;
+  const uint16_t* sl = static_cast<const uint16_t*>(slab_bf16);
+  uint16_t* o = static_cast<uint16_t*>(out_bf16);
+  if (use_small_copy(E, max_m, H / 8)) {
+    const unsigned blocks = small_blocks(E, max_m, H / 8);
+    if (weights != nullptr)
+      slab_to_expand_small_kernel<true><<<blocks, kSmallThreads, 0,
+                                          as_stream(stream)>>>(
+          sl, ld_slab, H, masked_m, psum, E, align, max_m, weights, o, ld_out,
+          out_rows);
+    else
+      slab_to_expand_small_kernel<false><<<blocks, kSmallThreads, 0,
+                                           as_stream(stream)>>>(
+          sl, ld_slab, H, masked_m, psum, E, align, max_m, nullptr, o, ld_out,
+          out_rows);
+    return launch_status();
+  }
   const CopyShape cs = copy_shape(E, max_m, H / 8);
   const int64_t rpb = cs.rows_per_block;
   const int64_t blocks = (int64_t)E * ceil_div(max_m, rpb);
   if (blocks > INT32_MAX || rpb * (H / 8) > (int64_t)INT32_MAX / 2)
     return MXQ_ERR_UNSUPPORTED;
-  const uint16_t* sl = static_cast<const uint16_t*>(slab_bf16);
-  uint16_t* o = static_cast<uint16_t*>(out_bf16);
   if (weights != nullptr)
     slab_to_expand_kernel<true><<<(unsigned)blocks, cs.threads, 0,
                                   as_stream(stream)>>>(

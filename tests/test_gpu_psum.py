@@ -183,3 +183,37 @@ def test_prefill_sized_slab(ora):
     ref = ora.masked_slab_to_expand(bf16_to_host(slab), host(mm), psum, align,
                                     max_m, weights=w, out=out0.copy())
     assert_equal(bf16_to_host(got), ref, "weighted expand, large slab")
+
+
+def test_small_slab_expert_limits(ora):
+    """Small slabs with 64 experts (one per lane of the unit kernels), with
+    empty experts, one over capacity and the source ending inside the last
+    range; then 65 experts, which take the per-expert block grid; both
+    directions, the bf16 one with weights."""
+    rng = np.random.default_rng(31)
+    for E in (64, 65):
+        counts = rng.integers(0, 13, size=E).tolist()
+        counts[1], counts[E - 2] = 0, 20            # max_m 16: bit 0
+        align, max_m, H = 16, 16, 1040              # 130 vectors of bf16
+        slab, mm, psum, total = slab_case(ora, counts, align, max_m, H,
+                                          src_rows=None)
+        w = np.random.default_rng(E).uniform(0.01, 1, total).astype(
+            np.float32)
+        out0 = np.full((total, H), 0x1234, np.uint16)
+        say("slab_to_expand E=%d" % E)
+        got = mxq.moe_masked_slab_to_expand(
+            slab, mm, i32(psum), max_m, align,
+            weights=torch.from_numpy(w).to(DEV), out=bf16_to_dev(out0))
+        ref = ora.masked_slab_to_expand(bf16_to_host(slab), host(mm), psum,
+                                        align, max_m, weights=w,
+                                        out=out0.copy())
+        assert_equal(bf16_to_host(got), ref, "weighted expand E=%d" % E)
+
+        def sc(t):
+            return np.random.default_rng(7).integers(100, 140, (t, 9),
+                                                     np.uint8)
+        slab_case(ora, counts, align, max_m, 4112, payload="fp8", scales=sc)
+        # the source ends two rows into the last non-empty range: bit 1
+        last = max(i for i, c in enumerate(counts) if c > 0)
+        short = psum[last] - 2 if last >= 0 else 0
+        slab_case(ora, counts, align, max_m, 64, src_rows=int(short))
