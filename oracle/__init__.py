@@ -23,7 +23,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mxq_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MXQ_ORACLE_LIB names a prebuilt copy to load instead (the sanitizer build
+# of oracle/sanitize.py); it is never rebuilt here.
+_LIB_ENV = os.environ.get("MXQ_ORACLE_LIB")
+_LIB_PATH = _LIB_ENV or os.path.join(_HERE, "liboracle.so")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -33,6 +36,10 @@ _p = ctypes.c_void_p
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (it is C, not part of the GPU library)."""
+    if _LIB_ENV:
+        if not os.path.exists(_LIB_ENV):
+            raise RuntimeError("MXQ_ORACLE_LIB=%s does not exist" % _LIB_ENV)
+        return _LIB_ENV
     if force or not os.path.exists(_LIB_PATH) or (
         os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
     ):
