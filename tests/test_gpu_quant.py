@@ -179,3 +179,26 @@ def test_live_rows_clip_and_g128(ora):
                       live_counts=[41, -2, 17])
     live_both(ora, lr, G=32)
     live_both(ora, lr, G=128)
+
+
+def test_live_rows_many_segments_and_ragged_chunks(ora):
+    """64 segments (the most the ballot path holds: one per lane), with
+    empty segments, clipped and negative counts, a hidden size that ends
+    inside a 1024-channel chunk, and every row of a small buffer live; then
+    65 segments, which take the row-per-block path."""
+    rng = np.random.default_rng(21)
+    live = rng.integers(-3, 9, size=64)
+    live[::7] = 0
+    live[5] = 100                       # clipped to rows_per_segment
+    lr = si.live_rows(num_segments=64, rows_per_segment=6, H=1152,
+                      live_counts=live.tolist())
+    live_both(ora, lr, G=32)
+    live_both(ora, lr, G=128)
+    lr = si.live_rows(num_segments=3, rows_per_segment=50, H=96,
+                      live_counts=[50, 50, 50])
+    live_both(ora, lr, G=32)
+    live = rng.integers(0, 5, size=65)
+    lr = si.live_rows(num_segments=65, rows_per_segment=4, H=256,
+                      live_counts=live.tolist())
+    live_both(ora, lr, G=32)
+    live_both(ora, lr, G=128)
