@@ -127,6 +127,18 @@ def test_requant_equal_bounds_below_448(ora):
         requant_both(ora, q, s)
 
 
+def test_requant_rows_of_several_batches(ora):
+    """Rows longer than one 4 KB batch of the rewrite pass (which loads the
+    next batch before storing the current one), with a byte tail, in place
+    and out of place; and rows shorter than 16 bytes."""
+    rng = np.random.default_rng(15)
+    for T, H, pad in ((700, 7168, 0), (333, 8200, 8), (64, 12296, 24),
+                      (50, 8, 8)):
+        q, s = si.per_token_fp8(rng, T, H)
+        requant_both(ora, q, s, ld_pad=pad)
+        requant_both(ora, q, s, ld_pad=pad, in_place=True)
+
+
 def test_requant_operation_order_cases(ora):
     """Rows where two other operation orders round to other bytes than R6's
     (built in test_oracle_paths): the kernel gives R6's bytes."""
