@@ -31,6 +31,7 @@ __all__ = [
     "moe_masked_slab_to_expand", "moe_scatter_rows", "upscale_fp8_to_bf16",
     "requant_weight_block_ue8m0", "mxq_mfma_scale_bytes", "mfma_scales",
     "mxq_copy16", "moe_layout_scatter_quant", "moe_layout_noalloc",
+    "mxq_gather_read16", "mxq_fill_rows16",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +94,9 @@ _SIGNATURES = {
     "mx_quant_live_rows_mfma": (_i32, [_p, _i64, _i32, _i64, _p, _i32, _i32,
                                        _i32, _p, _i64, _p, _i32, _p]),
     "mxq_copy16": (_i32, [_p, _p, _i64, _i32, _p]),
+    "mxq_gather_read16": (_i32, [_p, _i64, _i64, _p, _i64, _i32, _i64, _p,
+                                 _p]),
+    "mxq_fill_rows16": (_i32, [_p, _i64, _i64, _i64, ctypes.c_uint32, _p]),
     "moe_layout_scatter_quant": (_i32, [_p, _i64, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _i64, _p, _p, _p, _p, _p, _p, _p,
                                         _i64, _i32, _i32, _p, _i64, _p, _i64,
@@ -242,6 +246,47 @@ def mxq_copy16(src: torch.Tensor, dst: torch.Tensor,
                           src.numel() * src.element_size(), int(nontemporal),
                           _stream(src))
     _check("mxq_copy16", st)
+    return dst
+
+
+def mxq_gather_read16(rows: torch.Tensor, idx: torch.Tensor,
+                      sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Bandwidth reference: the combine's gather reads alone (see
+    ``mxq_gather_read16`` in mxq.h).  ``rows`` is a 2-D device tensor,
+    ``idx`` int32 [groups, group]; returns the per-group XOR words."""
+    _dev(rows, "rows")
+    _dev(idx, "idx", rows)
+    if rows.dim() != 2 or rows.stride(1) != 1:
+        raise ValueError("rows must be 2-D with contiguous rows")
+    if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32 [groups, group]")
+    G, g = idx.shape
+    es = rows.element_size()
+    if sink is None:
+        sink = torch.empty(G, dtype=torch.int32, device=rows.device)
+    _dev(sink, "sink", rows)
+    if sink.dtype != torch.int32 or sink.numel() < G or \
+            not sink.is_contiguous():
+        raise ValueError("sink must be contiguous int32 with >= groups entries")
+    st = lib().mxq_gather_read16(_ptr(rows), rows.stride(0) * es,
+                                 rows.shape[0], _ptr(idx), G, g,
+                                 rows.shape[1] * es, _ptr(sink),
+                                 _stream(rows))
+    _check("mxq_gather_read16", st)
+    return sink
+
+
+def mxq_fill_rows16(dst: torch.Tensor, pattern: int = 0) -> torch.Tensor:
+    """Bandwidth reference: the combine's row writes alone (see
+    ``mxq_fill_rows16`` in mxq.h); fills the 2-D device tensor ``dst``."""
+    _dev(dst, "dst")
+    if dst.dim() != 2 or dst.stride(1) != 1:
+        raise ValueError("dst must be 2-D with contiguous rows")
+    es = dst.element_size()
+    st = lib().mxq_fill_rows16(_ptr(dst), dst.stride(0) * es, dst.shape[0],
+                               dst.shape[1] * es, pattern & 0xFFFFFFFF,
+                               _stream(dst))
+    _check("mxq_fill_rows16", st)
     return dst
 
 

@@ -334,6 +334,24 @@ mxq_status mx_quant_live_rows_mfma(const void* x_bf16, int64_t ld_x,
 mxq_status mxq_copy16(const void* src, void* dst, int64_t bytes,
                       int32_t nontemporal, void* stream);
 
+/* Bandwidth reference, not a step of the path: the combine's reads alone.
+ * Block g (g < groups) reads rows idx[g*group + j], j < group (entries
+ * outside [0, num_rows) are skipped), row_bytes bytes each (a multiple of
+ * 16) at row stride ld (bytes, a multiple of 16; rows 16-byte aligned),
+ * with the combine's pattern: a lane loads 16 bytes of each of the group's
+ * rows, all in flight, non-temporal.  sink[g] (device uint32 [groups])
+ * receives the XOR of the 32-bit words the block read.  1 <= group <= 64. */
+mxq_status mxq_gather_read16(const void* rows, int64_t ld, int64_t num_rows,
+                             const int32_t* idx, int64_t groups, int32_t group,
+                             int64_t row_bytes, uint32_t* sink, void* stream);
+
+/* Bandwidth reference, not a step of the path: the combine's writes alone.
+ * Writes `pattern` to every 32-bit word of rows [0, rows) of dst (row_bytes
+ * each, a multiple of 16, at row stride ld bytes; 16-byte aligned), one
+ * block per row, 16-byte streaming stores. */
+mxq_status mxq_fill_rows16(void* dst, int64_t ld, int64_t rows,
+                           int64_t row_bytes, uint32_t pattern, void* stream);
+
 /* ------------------------------------------------------------- requant */
 
 /* Per-token scaled fp8 -> one per-tensor scale [P2 impl. items 1-2].

@@ -150,6 +150,20 @@ def test_copy16_validation(mxq):
     assert L.mxq_copy16(FAKE + 8, FAKE + 4096, 32, 0, None) == INVALID
     assert L.mxq_copy16(FAKE, FAKE + 4096, 32, 4, None) == INVALID
     assert L.mxq_copy16(FAKE, FAKE + 4096, 32, -1, None) == INVALID
+    # the gather-read and row-fill references
+    g = L.mxq_gather_read16
+    assert g(FAKE, 64, 10, FAKE, 0, 8, 64, FAKE, None) == 0      # no groups
+    assert g(FAKE, 64, 10, FAKE, 4, 0, 64, FAKE, None) == INVALID
+    assert g(FAKE, 64, 10, FAKE, 4, 65, 64, FAKE, None) == INVALID
+    assert g(FAKE, 64, 10, FAKE, 4, 8, 72, FAKE, None) == INVALID  # ld < row
+    assert g(FAKE, 64, 10, FAKE, 4, 8, 40, FAKE, None) == INVALID  # not 16
+    assert g(FAKE + 8, 64, 10, FAKE, 4, 8, 64, FAKE, None) == INVALID
+    assert g(FAKE, 64, 10, None, 4, 8, 64, FAKE, None) == INVALID
+    f = L.mxq_fill_rows16
+    assert f(FAKE, 64, 0, 64, 0, None) == 0
+    assert f(FAKE, 48, 3, 64, 0, None) == INVALID
+    assert f(FAKE + 8, 64, 3, 64, 0, None) == INVALID
+    assert f(None, 64, 3, 64, 0, None) == INVALID
 
 
 def test_mfma_placement_validation(mxq):
