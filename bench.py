@@ -80,10 +80,19 @@ def bytes_combine(T, K, H, assignments, out_bytes=2):
 
 # ---------------------------------------------------------------- helpers
 
-def time_calls(torch, fn, reps=20, warmup=3, replays=5):
-    """GPU time per call of fn, in microseconds: reps calls captured in one
-    hipGraph, timed with events around each replay (median of replays), so
-    host launch cost between calls is not counted."""
+def spread(samples):
+    """Median, 10th and 90th percentile of a list of times (or rates)."""
+    a = np.asarray(samples, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 2),
+            "median": round(float(np.median(a)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2),
+            "n": int(a.size)}
+
+
+def time_calls_samples(torch, fn, reps=20, warmup=3, replays=100):
+    """GPU time per call of fn, in microseconds, one sample per replay: reps
+    calls captured in one hipGraph, timed with events around each replay,
+    so host launch cost between calls is not counted."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -93,26 +102,31 @@ def time_calls(torch, fn, reps=20, warmup=3, replays=5):
             fn()
     g.replay()
     torch.cuda.synchronize()
-    per = []
     hs = torch.cuda.current_stream().cuda_stream
-    ev = HipEvents(2)
-    for _ in range(replays):
-        ev.record(0, hs)
+    ev = HipEvents(2 * replays)
+    for i in range(replays):
+        ev.record(2 * i, hs)
         g.replay()
-        ev.record(1, hs)
-        torch.cuda.synchronize()
-        per.append(ev.ms(0, 1) / reps)
+        ev.record(2 * i + 1, hs)
+    torch.cuda.synchronize()
+    per = [ev.ms(2 * i, 2 * i + 1) / reps * 1e3 for i in range(replays)]
     ev.close()
     del g
-    return float(np.median(per)) * 1e3
+    return per
 
 
-def time_calls_cold(torch, fn, flush, reps=10, warmup=2):
+def time_calls(torch, fn, reps=20, warmup=3, replays=100):
+    """Median of time_calls_samples."""
+    return float(np.median(time_calls_samples(torch, fn, reps, warmup,
+                                              replays)))
+
+
+def time_calls_cold_samples(torch, fn, flush, reps=100, warmup=2):
     """GPU time per call of fn with the 256 MB last-level cache (MALL) and
     the L2s flushed before each call by reading `flush` (512 MB, written
     once beforehand, so the evicting lines are clean and nothing is written
-    back during the call): events bracket the call alone; median over
-    reps."""
+    back during the call): events bracket the call alone; one sample per
+    call, in microseconds."""
     for _ in range(warmup):
         fn()
     flush_f = flush.view(torch.float32)
@@ -125,9 +139,38 @@ def time_calls_cold(torch, fn, flush, reps=10, warmup=2):
         fn()
         ev.record(2 * i + 1, hs)
     torch.cuda.synchronize()
-    per = [ev.ms(2 * i, 2 * i + 1) for i in range(reps)]
+    per = [ev.ms(2 * i, 2 * i + 1) * 1e3 for i in range(reps)]
     ev.close()
-    return float(np.median(per)) * 1e3
+    return per
+
+
+def time_calls_cold(torch, fn, flush, reps=100, warmup=2):
+    """Median of time_calls_cold_samples."""
+    return float(np.median(time_calls_cold_samples(torch, fn, flush, reps,
+                                                   warmup)))
+
+
+def timed_row(torch, fn, nbytes=None, units=None, unit_name=None, reps=20,
+              replays=100, flush=None):
+    """A row's record: median time per call with its 10-90 % spread over
+    `replays` graph replays (and over as many calls with the MALL flushed
+    when `flush` is given), plus GB/s of `nbytes` and `unit_name`/s."""
+    per = time_calls_samples(torch, fn, reps=reps, replays=replays)
+    us = float(np.median(per))
+    r = {"us": round(us, 2), "us_spread": spread(per)}
+    if nbytes is not None:
+        r["algorithmic_bytes"] = nbytes
+        r["gbs"] = round(nbytes / (us * 1e-6) / 1e9, 2)
+    if units is not None:
+        r[unit_name + "_per_s"] = round(units / (us * 1e-6), 1)
+    if flush is not None:
+        cold = time_calls_cold_samples(torch, fn, flush)
+        cu = float(np.median(cold))
+        r["cold_us"] = round(cu, 2)
+        r["cold_us_spread"] = spread(cold)
+        if nbytes is not None:
+            r["cold_gbs"] = round(nbytes / (cu * 1e-6) / 1e9, 2)
+    return r
 
 
 class HipEvents:
@@ -360,11 +403,13 @@ def main():
     if status != 0:
         raise RuntimeError("a library call in the event-free pass failed")
 
-    # per-kernel pass: the same steps with events around each kernel
-    kev = HipEvents(4 * args.steps)
+    # per-kernel pass: the same steps with events around each kernel, at
+    # least 100 of them whatever --steps is, for the spread of each kernel
+    n_k = max(args.steps, 100)
+    kev = HipEvents(4 * n_k)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(n_k):
         status |= kev.record(4 * i, hs)
         status |= L.moe_layout(*lay_args)
         status |= kev.record(4 * i + 1, hs)
@@ -373,14 +418,15 @@ def main():
         status |= L.moe_combine(*cb_args)
         status |= kev.record(4 * i + 3, hs)
     torch.cuda.synchronize()
-    kev_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kev_step_ms = (time.perf_counter() - t0) * 1e3 / n_k
     if status != 0:
         raise RuntimeError("a library call in the per-kernel pass failed")
-    k_ms = [[kev.ms(4 * i + k, 4 * i + k + 1) for i in range(args.steps)]
+    k_us = [[kev.ms(4 * i + k, 4 * i + k + 1) * 1e3 for i in range(n_k)]
             for k in range(3)]
     kev.close()
-    lay_ms, sq_ms, kcb_ms = k_ms
-    ev_step_ms = float(np.mean(lay_ms) + np.mean(sq_ms) + np.mean(kcb_ms))
+    lay_us, sq_us, kcb_us = k_us
+    ev_step_ms = float(np.mean(lay_us) + np.mean(sq_us) +
+                       np.mean(kcb_us)) / 1e3
 
     # the same step captured once in a hipGraph and replayed (no per-kernel
     # host launch cost); reported beside the eager timed region
@@ -390,10 +436,10 @@ def main():
     # flushed before each step by reading 512 MB, so that every input comes
     # from HBM (in the loop above the token rows stay cached from the
     # previous step, since the combine's loads and stores bypass the
-    # cache); events bracket the step's kernels alone.
+    # cache); events bracket the step's kernels alone.  100 steps.
     flush = torch.zeros(512 << 20, dtype=torch.uint8,
                         device=dev).view(torch.float32)
-    n_cold = min(args.steps, 20)
+    n_cold = 100
     evc = HipEvents(4 * n_cold)
     torch.cuda.synchronize()
     for i in range(n_cold):
@@ -408,18 +454,43 @@ def main():
     torch.cuda.synchronize()
     if status != 0:
         raise RuntimeError("a library call in the flushed loop failed")
-    del flush
-    cold = [float(np.mean([evc.ms(4 * i + k, 4 * i + k + 1)
-                           for i in range(n_cold)])) for k in range(3)]
+    cold_us = [[evc.ms(4 * i + k, 4 * i + k + 1) * 1e3 for i in range(n_cold)]
+               for k in range(3)]
     evc.close()
+
+    # The combine's two halves alone, in this run: its gather reads (the
+    # same 65536 rows through the same src2dst, non-temporal loads) and its
+    # 117 MB of output rows written with streaming stores; their sum is the
+    # time the combine would take if its reads and writes simply added up.
+    gather_sink = torch.empty(T, dtype=torch.int32, device=dev)
+    s2d = lay_out["src2dst"]
+    gather_us = time_calls_samples(
+        torch, lambda: mxq.mxq_gather_read16(y, s2d, gather_sink))
+    write_us = time_calls_samples(torch, lambda: mxq.mxq_fill_rows16(out))
+    comb_us_graph = time_calls_samples(
+        torch, lambda: mxq.moe_combine(y, s2d, w, out=out))
+    # the same three with the MALL flushed before each call
+    gather_cold = time_calls_cold_samples(
+        torch, lambda: mxq.mxq_gather_read16(y, s2d, gather_sink), flush)
+    write_cold = time_calls_cold_samples(
+        torch, lambda: mxq.mxq_fill_rows16(out), flush)
+    del flush
 
     value = B_step / (step_ms * 1e-3) / 1e9
     cb_gbs = B_cb / (np.mean(cb_ms) * 1e-3) / 1e9
-    sq_gbs = B_sq / (np.mean(sq_ms) * 1e-3) / 1e9
-    kcb_gbs = B_cb / (np.mean(kcb_ms) * 1e-3) / 1e9
-    sqcb_gbs = ((B_sq + B_cb) / ((np.mean(sq_ms) + np.mean(kcb_ms)) * 1e-3)
-                / 1e9)
+    sq_gbs = B_sq / (np.median(sq_us) * 1e-6) / 1e9
+    kcb_gbs = B_cb / (np.median(kcb_us) * 1e-6) / 1e9
+    sqcb_gbs = ((B_sq + B_cb) / ((np.median(sq_us) + np.median(kcb_us)) *
+                                 1e-6) / 1e9)
+    # per flushed step: scatter+combine as a fraction of the 8 TB/s peak
+    frac_cold = [(B_sq + B_cb) / ((a + c) * 1e-6) / 1e9 / PEAK_HBM_GBS
+                 for a, c in zip(cold_us[1], cold_us[2])]
+    frac_warm = [(B_sq + B_cb) / ((a + c) * 1e-6) / 1e9 / PEAK_HBM_GBS
+                 for a, c in zip(sq_us, kcb_us)]
+    cold_med = [float(np.median(c)) for c in cold_us]
     traffic = traffic_record()
+    g_med, w_med = float(np.median(gather_us)), float(np.median(write_us))
+    c_med = float(np.median(comb_us_graph))
 
     result = {
         "metric": METRIC,
@@ -449,27 +520,33 @@ def main():
         "graph_replay": {"ms_per_step": round(graph_ms, 4),
                          "gbs": round(B_step / (graph_ms * 1e-3) / 1e9, 2)},
         "timing": "value: wall clock over the timed steps, bracketed by "
-                  "device synchronizations; HIP events (system fence "
-                  "disabled) on the launch stream around each step's "
+                  "device synchronizations, with the token rows still in "
+                  "the MALL from the previous step; HIP events (system "
+                  "fence disabled) on the launch stream around each step's "
                   "combine in the same loop give the roofline; the "
-                  "per-kernel pass repeats the steps with events around "
-                  "every kernel",
+                  "per-kernel pass (>= 100 steps) and the MALL-flushed pass "
+                  "(100 steps) bracket every kernel; spreads are the 10th, "
+                  "50th and 90th percentiles over those samples",
         "moe_combine_us_in_timed_region": round(
             1e3 * float(np.mean(cb_ms)), 2),
         "ms_per_step_without_events": round(noev_step_ms, 4),
         "scatter_quant_plus_combine": {
             "bytes": B_sq + B_cb,
-            "us": round(1e3 * (np.mean(sq_ms) + np.mean(kcb_ms)), 2),
+            "us": round(float(np.median(sq_us) + np.median(kcb_us)), 2),
             "gbs": round(sqcb_gbs, 2),
             "pct_of_peak": round(100 * sqcb_gbs / PEAK_HBM_GBS, 2),
+            "pct_of_peak_spread": spread([100 * f for f in frac_warm]),
         },
         "kernels_us": {
-            "moe_layout": round(1e3 * float(np.mean(lay_ms)), 2),
-            "moe_scatter_quant": round(1e3 * float(np.mean(sq_ms)), 2),
-            "moe_combine": round(1e3 * float(np.mean(kcb_ms)), 2),
+            "moe_layout": round(float(np.median(lay_us)), 2),
+            "moe_scatter_quant": round(float(np.median(sq_us)), 2),
+            "moe_combine": round(float(np.median(kcb_us)), 2),
             "event_sum_per_step": round(1e3 * ev_step_ms, 2),
             "ms_per_step_with_these_events": round(kev_step_ms, 4),
         },
+        "kernels_us_spread": {"moe_layout": spread(lay_us),
+                              "moe_scatter_quant": spread(sq_us),
+                              "moe_combine": spread(kcb_us)},
         "kernels_gbs": {"moe_scatter_quant": round(sq_gbs, 2),
                         "moe_combine": round(kcb_gbs, 2)},
         "algorithmic_bytes": {"moe_layout": B_lay, "moe_scatter_quant": B_sq,
@@ -477,17 +554,22 @@ def main():
         "step_mall_flushed": {
             "note": "the MALL and L2s flushed (512 MB read) before each "
                     "step; HIP events around the step's kernels; "
-                    "%d steps" % n_cold,
-            "ms_per_step": round(sum(cold), 4),
-            "gbs": round(B_step / (sum(cold) * 1e-3) / 1e9, 2),
+                    "%d steps, medians" % n_cold,
+            "ms_per_step": round(sum(cold_med) / 1e3, 4),
+            "gbs": round(B_step / (sum(cold_med) * 1e-6) / 1e9, 2),
             "pct_of_peak": round(
-                100 * B_step / (sum(cold) * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-            "kernels_us": {"moe_layout": round(1e3 * cold[0], 2),
-                           "moe_scatter_quant": round(1e3 * cold[1], 2),
-                           "moe_combine": round(1e3 * cold[2], 2)},
+                100 * B_step / (sum(cold_med) * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                2),
+            "kernels_us": {"moe_layout": round(cold_med[0], 2),
+                           "moe_scatter_quant": round(cold_med[1], 2),
+                           "moe_combine": round(cold_med[2], 2)},
+            "kernels_us_spread": {"moe_layout": spread(cold_us[0]),
+                                  "moe_scatter_quant": spread(cold_us[1]),
+                                  "moe_combine": spread(cold_us[2])},
             "scatter_quant_plus_combine_pct_of_peak": round(
-                100 * (B_sq + B_cb) / ((cold[1] + cold[2]) * 1e-3) / 1e9 /
-                PEAK_HBM_GBS, 2),
+                100 * float(np.median(frac_cold)), 2),
+            "scatter_quant_plus_combine_pct_of_peak_spread": spread(
+                [100 * f for f in frac_cold]),
         },
         "box_copy_gbs": round(copy_gbs, 1),
         "box_copy16_kernel_gbs": copy16,
@@ -499,6 +581,34 @@ def main():
             "unit": "GB/s",
             "frac": round(cb_gbs / PEAK_HBM_GBS, 4),
             "traffic": traffic,
+            # the target as the pages' workload defines it: scatter+quant
+            # plus combine at the prefill shape, against the 8 TB/s peak
+            "target_scatter_quant_plus_combine": {
+                "frac_warm": round(float(np.median(frac_warm)), 4),
+                "frac_mall_flushed": round(float(np.median(frac_cold)), 4),
+                "frac_mall_flushed_p10": round(
+                    float(np.percentile(frac_cold, 10)), 4),
+                "frac_mall_flushed_p90": round(
+                    float(np.percentile(frac_cold, 90)), 4),
+            },
+            # the combine beside its own two halves measured in this run
+            "combine_same_run_halves": {
+                "gather_read_us": round(g_med, 2),
+                "gather_read_gbs": round(
+                    (A * H * 2 + T * K * 4) / (g_med * 1e-6) / 1e9, 2),
+                "output_write_us": round(w_med, 2),
+                "output_write_gbs": round(T * H * 2 / (w_med * 1e-6) / 1e9,
+                                          2),
+                "sum_us": round(g_med + w_med, 2),
+                "combine_us": round(c_med, 2),
+                "combine_over_sum": round(c_med / (g_med + w_med), 4),
+                "gather_read_cold_us": round(float(np.median(gather_cold)),
+                                             2),
+                "output_write_cold_us": round(float(np.median(write_cold)),
+                                              2),
+                "note": "graph-timed medians over 100 replays of 20 calls; "
+                        "cold: MALL flushed before each call",
+            },
         },
     }
     variants = srows = None
@@ -510,11 +620,15 @@ def main():
     del q, s, out
 
     if not args.no_rows:
-        result["rows"] = other_rows(torch, mxq, si, dev)
+        result["rows"] = other_rows(torch, mxq, si, dev,
+                                    cpu=not args.no_cpu)
         result["rows"]["timing"] = ("each row: GPU time per call, 20 calls "
-                                    "captured in a hipGraph, median of 5 "
-                                    "replays; cold variants flush the MALL "
-                                    "before each eager call")
+                                    "captured in a hipGraph, median and "
+                                    "10-90 % spread over 100 replays; cold "
+                                    "variants flush the MALL before each of "
+                                    "100 eager calls; cpu_baseline: the "
+                                    "oracle on this host's cores, median of "
+                                    "3, and on one thread")
         result["rows"]["scale_variants"] = variants
         result["rows"]["scatter_rows"] = srows
 
@@ -567,11 +681,11 @@ def layout_sweep(torch, mxq, si, dev, H=7168, K=8):
                 o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
                 t_l = time_calls(torch, lambda: mxq.moe_layout(
                     ids, 0, e_loc, kind, capacity=cap, num_rows=rows,
-                    out=lay))
+                    out=lay), replays=10)
                 t_s = time_calls(torch, lambda: mxq.moe_scatter_quant(
-                    x, lay["src2dst"], rows, q=q, scales=sc))
+                    x, lay["src2dst"], rows, q=q, scales=sc), replays=10)
                 t_c = time_calls(torch, lambda: mxq.moe_combine(
-                    y, lay["src2dst"], w, out=o))
+                    y, lay["src2dst"], w, out=o), replays=10)
                 pt[kind] = {"rows": rows,
                             "buffer_gib": round(rows * H * 3 / 2 ** 30, 2),
                             "layout_us": round(t_l, 2),
@@ -686,7 +800,43 @@ def scatter_rows_row(torch, mxq, x, src2dst, R, H, q, T, K, A, dev):
             "gbs": round(byts / (us * 1e-6) / 1e9, 2)}
 
 
-def other_rows(torch, mxq, si, dev):
+def cpu_row(fn, nbytes=None, units=None, unit_name=None, repeats=3,
+            cpu=True):
+    """The oracle timed on this host's cores beside a GPU row: wall clock,
+    median of `repeats` runs on every OpenMP thread, then one run on one
+    thread.  Returns None when the CPU leg is off."""
+    if not cpu:
+        return None
+    import oracle
+    cores = oracle.max_threads()
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        fn()
+        t1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(cores)
+    r = {"kind": "oracle", "cores": cores, "seconds": round(t, 5),
+         "single_thread_seconds": round(t1, 5)}
+    if nbytes is not None:
+        r["gbs"] = round(nbytes / t / 1e9, 4)
+        r["single_thread_gbs"] = round(nbytes / t1 / 1e9, 4)
+    if units is not None:
+        r[unit_name + "_per_s"] = round(units / t, 1)
+        r["single_thread_" + unit_name + "_per_s"] = round(units / t1, 1)
+    return r
+
+
+def other_rows(torch, mxq, si, dev, cpu=True):
+    import_oracle = cpu
+    if import_oracle:
+        import oracle
     rows = {}
     flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -705,54 +855,81 @@ def other_rows(torch, mxq, si, dev):
     touched_d = int(loc_mask.any(axis=1).sum())
     b_sq_d = bytes_scatter(touched_d, d.T, d.K, d.H, 128, loc)
     b_cb_d = bytes_combine(d.T, d.K, d.H, loc)
-    us_l = time_calls(torch, lambda: mxq.moe_layout(
+    r_l = timed_row(torch, lambda: mxq.moe_layout(
         ids, 0, 32, "masked", capacity=128, out=lay))
-    us_s = time_calls(torch, lambda: mxq.moe_scatter_quant(
+    r_s = timed_row(torch, lambda: mxq.moe_scatter_quant(
         x, lay["src2dst"], R, q=q, scales=s))
-    us_c = time_calls(torch, lambda: mxq.moe_combine(yv, lay["src2dst"], w))
+    r_c = timed_row(torch, lambda: mxq.moe_combine(yv, lay["src2dst"], w))
 
     def layout_then_scatter():
         mxq.moe_layout(ids, 0, 32, "masked", capacity=128, out=lay)
         mxq.moe_scatter_quant(x, lay["src2dst"], R, q=q, scales=s)
-    us_ls = time_calls(torch, layout_then_scatter)
-    us_f = time_calls(torch, lambda: mxq.moe_layout_scatter_quant(
+    r_ls = timed_row(torch, layout_then_scatter)
+    r_f = timed_row(torch, lambda: mxq.moe_layout_scatter_quant(
         ids, x, 0, 32, "masked", capacity=128, out=lay, q=q, scales=s))
+    us_l, us_s, us_c, us_f = r_l["us"], r_s["us"], r_c["us"], r_f["us"]
     rows["decode_masked"] = {
         "workload": "T=128, hidden 7168, experts [0,32) of 256 local, top-8, "
                     "slab capacity 128, UE8M0 group-128",
-        "local_assignments": loc, "layout_us": round(us_l, 2),
-        "scatter_quant_us": round(us_s, 2), "combine_us": round(us_c, 2),
-        "layout_then_scatter_quant_us": round(us_ls, 2),
-        "fused_layout_scatter_quant_us": round(us_f, 2),
+        "local_assignments": loc, "layout_us": us_l,
+        "scatter_quant_us": us_s, "combine_us": us_c,
+        "layout_then_scatter_quant_us": r_ls["us"],
+        "fused_layout_scatter_quant_us": us_f,
+        "us_spread": {"layout": r_l["us_spread"],
+                      "scatter_quant": r_s["us_spread"],
+                      "combine": r_c["us_spread"],
+                      "fused_layout_scatter_quant": r_f["us_spread"]},
         "assignments_per_s": round(loc / ((us_l + us_s + us_c) * 1e-6), 1),
         "assignments_per_s_fused": round(loc / ((us_f + us_c) * 1e-6), 1),
         "scatter_quant_bytes": b_sq_d, "combine_bytes": b_cb_d,
         "note": "latency-bound: %.2f MB and %.2f MB move in the scatter and "
                 "the combine" % (b_sq_d / 1e6, b_cb_d / 1e6)}
+    if cpu:
+        yv_h = yv.view(torch.int16).cpu().numpy().view(np.uint16)
+
+        def ora_decode():
+            ol = oracle.moe_layout(d.topk_ids, 0, 32, "masked",
+                                   capacity=128)
+            oracle.scatter_quant(d.x, ol["src2dst"], 128, R)
+            oracle.combine(yv_h, ol["src2dst"], d.topk_weights)
+        rows["decode_masked"]["cpu_baseline"] = cpu_row(
+            ora_decode, nbytes=b_sq_d + b_cb_d, units=loc,
+            unit_name="assignments")
+        rows["decode_masked"]["cpu_baseline"]["sample"] = (
+            "the whole decode batch: layout + scatter_quant + combine")
 
     # send-side MX quant over live rows: 24576 x 7168 padded, 112 live
     xs = si.gaussian_bf16_device(404, (24576, 7168), dev)
     qs = torch.empty((24576, 7168), dtype=torch.uint8, device=dev)
     ss = torch.empty((24576, 224), dtype=torch.uint8, device=dev)
     res = {}
+    xs_h = xs.view(torch.int16).cpu().numpy().view(np.uint16) if cpu else None
+    qs_h = np.zeros((24576, 7168), np.uint8) if cpu else None
+    ss_h = np.zeros((24576, 224), np.uint8) if cpu else None
     for name, live in (("14x8", [14] * 8), ("112+0x7", [112] + [0] * 7),
                        ("empty", [0] * 8)):
         lc = torch.tensor(live, dtype=torch.int32, device=dev)
-        us = time_calls(torch, lambda: mxq.mx_quant_live_rows(
-            xs, 8, lc, q=qs, scales=ss))
         n = sum(live)
         byts = n * (7168 * 2 + 7168 + 224) + 32
-        res[name] = {"live_rows": n, "us": round(us, 2),
-                     "rows_per_s": round(n / (us * 1e-6), 1),
-                     "algorithmic_bytes": byts}
+        res[name] = dict(live_rows=n, **timed_row(
+            torch, lambda: mxq.mx_quant_live_rows(xs, 8, lc, q=qs, scales=ss),
+            nbytes=byts, units=n, unit_name="rows"))
+        if cpu:
+            live_h = np.asarray(live, np.int32)
+            res[name]["cpu_baseline"] = cpu_row(
+                lambda: oracle.mx_quant_live_rows(xs_h, 8, live_h, 32,
+                                                  qs_h, ss_h),
+                nbytes=byts, units=n, unit_name="rows")
+            res[name]["cpu_baseline"]["sample"] = "the same %d live rows" % n
     res["padded_grid_equivalent_bytes"] = 24576 * (7168 * 2 + 7168 + 224)
     # the same quant over every row of the padded buffer (what a receiver
     # that sizes its grid by the buffer pays)
     lc = torch.full((8,), 3072, dtype=torch.int32, device=dev)
-    us_pad = time_calls(torch, lambda: mxq.mx_quant_live_rows(
+    pad = timed_row(torch, lambda: mxq.mx_quant_live_rows(
         xs, 8, lc, q=qs, scales=ss), reps=5)
-    res["padded_grid_us"] = round(us_pad, 2)
-    res["padded_over_live_14x8"] = round(us_pad / res["14x8"]["us"], 1)
+    res["padded_grid_us"] = pad["us"]
+    res["padded_grid_us_spread"] = pad["us_spread"]
+    res["padded_over_live_14x8"] = round(pad["us"] / res["14x8"]["us"], 1)
     # the same 14x8 live rows with the scales in the block-scaled MFMA
     # placement (32-row tiles)
     lc = torch.tensor([14] * 8, dtype=torch.int32, device=dev)
@@ -760,10 +937,14 @@ def other_rows(torch, mxq, si, dev):
     us = time_calls(torch, lambda: mxq.mx_quant_live_rows_ex(
         xs, 8, lc, "e8m0_g32", scale_layout="mfma32", q=qs, scales=sm))
     res["14x8_mfma32_us"] = round(us, 2)
+    # an empty kernel launched the same way: what one launch costs here
+    res["note"] = ("a launch costs about 2.1 us per call in this timing "
+                   "(measured with an empty kernel), the floor of the "
+                   "empty batch")
     res["workload"] = ("24576 x 7168 bf16 padded buffer = 8 segments of "
                        "3072 rows, e8m0 group-32 (224 scales/row)")
     rows["live_rows_mx"] = res
-    del xs, qs, ss
+    del xs, qs, ss, xs_h, qs_h, ss_h
 
     # per-token -> per-tensor requant, 16384 x 4096
     rb = si.requant_input()
@@ -773,31 +954,31 @@ def other_rows(torch, mxq, si, dev):
     Sd = torch.empty(1, dtype=torch.float32, device=dev)
     rws = torch.empty(mxq.requant_workspace_bytes(*qi.shape),
                       dtype=torch.uint8, device=dev)
-    us = time_calls(torch, lambda: mxq.requant_per_token_to_per_tensor(
-        qi, sc, q_out=qo, tensor_scale=Sd, workspace=rws))
     byts = 2 * qi.numel() + qi.shape[0] * 4 + 4
-    us_cold = time_calls_cold(torch, lambda: mxq.requant_per_token_to_per_tensor(
-        qi, sc, q_out=qo, tensor_scale=Sd, workspace=rws), flush)
-    # worst case of the max pass: equal token scales, so no row can be
-    # skipped and pass 1 reads the whole input
+    rq = timed_row(torch, lambda: mxq.requant_per_token_to_per_tensor(
+        qi, sc, q_out=qo, tensor_scale=Sd, workspace=rws), nbytes=byts,
+        flush=flush)
+    # every token scale equal (2^-3): every row's bound is the largest
     sc_eq = torch.full_like(sc, 2.0 ** -3)
-    us_eq = time_calls(torch, lambda: mxq.requant_per_token_to_per_tensor(
-        qi, sc_eq, q_out=qo, tensor_scale=Sd, workspace=rws))
+    rq_eq = timed_row(torch, lambda: mxq.requant_per_token_to_per_tensor(
+        qi, sc_eq, q_out=qo, tensor_scale=Sd, workspace=rws), nbytes=byts)
     rows["requant"] = {"workload": "16384 x 4096 fp8, per-token scales "
-                                   "2^U, U~U[-8,4]",
-                       "us": round(us, 2), "algorithmic_bytes": byts,
-                       "gbs": round(byts / (us * 1e-6) / 1e9, 2),
-                       "cold_us": round(us_cold, 2),
-                       "cold_gbs": round(byts / (us_cold * 1e-6) / 1e9, 2),
-                       "equal_scales_us": round(us_eq, 2),
-                       "equal_scales_gbs": round(byts / (us_eq * 1e-6) / 1e9,
-                                                 2),
+                                   "2^U, U~U[-8,4]", **rq,
+                       "equal_scales_us": rq_eq["us"],
+                       "equal_scales_gbs": rq_eq["gbs"],
+                       "equal_scales_us_spread": rq_eq["us_spread"],
                        "note": "warm: the 64 MiB input stays in the 256 MB "
                                "MALL across the two passes and back-to-back "
                                "calls; cold: MALL flushed by reading 512 MB "
                                "before each call; equal_scales: every token "
-                               "scale 2^-3, so the max pass cannot skip a "
-                               "row (warm)"}
+                               "scale 2^-3, so every row's bound is the "
+                               "largest (rows holding 448 settle the max "
+                               "pass at once) (warm)"}
+    if cpu:
+        rows["requant"]["cpu_baseline"] = cpu_row(
+            lambda: oracle.requant_per_token_to_per_tensor(rb.q, rb.scales),
+            nbytes=byts, units=qi.shape[0], unit_name="rows")
+        rows["requant"]["cpu_baseline"]["sample"] = "the whole 16384 x 4096"
     del qi, qo
 
     # psum (expanded) layout repack at the decode shape: the dispatcher's
@@ -812,7 +993,8 @@ def other_rows(torch, mxq, si, dev):
     xsc = torch.randint(100, 140, (total, 56), dtype=torch.uint8, device=dev)
     slab = torch.empty((32 * 128, 7168), dtype=torch.uint8, device=dev)
     slab_s = torch.empty((32 * 128, 56), dtype=torch.uint8, device=dev)
-    us_e = time_calls(torch, lambda: mxq.moe_expand_to_masked_slab(
+    real = int(cnt.sum())
+    r_e = timed_row(torch, lambda: mxq.moe_expand_to_masked_slab(
         xr, psum, 128, 128, scales=xsc, slab=slab, slab_scales=slab_s))
     _, _, mm, _ = mxq.moe_expand_to_masked_slab(xr, psum, 128, 128,
                                                  scales=xsc, slab=slab,
@@ -820,17 +1002,18 @@ def other_rows(torch, mxq, si, dev):
     ys = si.gaussian_bf16_device(206, (32 * 128, 7168), dev)
     wexp = torch.rand(total, device=dev)
     oexp = torch.zeros((total, 7168), dtype=torch.bfloat16, device=dev)
-    us_b = time_calls(torch, lambda: mxq.moe_masked_slab_to_expand(
+    r_b = timed_row(torch, lambda: mxq.moe_masked_slab_to_expand(
         ys, mm, psum, 128, 128, weights=wexp, out=oexp))
     us_m = time_calls(torch, lambda: mxq.moe_m_indices_from_psum(
         psum, total, 128))
-    real = int(cnt.sum())
     rows["psum_repack"] = {
         "workload": "decode expanded layout: %d real rows in %d (32 experts, "
                     "128-aligned) <-> slab [32, 128, 7168]" % (real, total),
-        "expand_to_masked_slab_us": round(us_e, 2),
+        "expand_to_masked_slab_us": r_e["us"],
+        "expand_to_masked_slab_us_spread": r_e["us_spread"],
         "expand_bytes": real * 2 * (7168 + 56) + 32 * 8,
-        "masked_slab_to_expand_us": round(us_b, 2),
+        "masked_slab_to_expand_us": r_b["us"],
+        "masked_slab_to_expand_us_spread": r_b["us_spread"],
         "slab_to_expand_bytes": real * (2 * 7168 * 2 + 4),
         "m_indices_from_psum_us": round(us_m, 2)}
     del xr, xsc, slab, slab_s, ys, oexp
@@ -846,8 +1029,10 @@ def other_rows(torch, mxq, si, dev):
         np.random.default_rng(si.SEEDS["fp8_dispatch"]),
         (rows_u, H_u // 128))).to(dev)
     ou = torch.empty((rows_u, H_u), dtype=torch.bfloat16, device=dev)
-    us = time_calls(torch, lambda: mxq.upscale_fp8_to_bf16(qu, su, n_u,
-                                                          out=ou))
+    byts = n_u * (H_u + 4 * (H_u // 128) + 2 * H_u)
+    up = timed_row(torch, lambda: mxq.upscale_fp8_to_bf16(qu, su, n_u,
+                                                         out=ou),
+                   nbytes=byts)
     # the same calls writing three output buffers in turn (3 x 117 MB, more
     # than the 256 MB MALL), so each call's output reaches HBM during the
     # following calls instead of being overwritten in the cache
@@ -858,12 +1043,9 @@ def other_rows(torch, mxq, si, dev):
         turn[0] += 1
         mxq.upscale_fp8_to_bf16(qu, su, n_u, out=ous[turn[0] % 3])
     us_rot = time_calls(torch, up_rot, reps=21)
-    byts = n_u * (H_u + 4 * (H_u // 128) + 2 * H_u)
     rows["upscale"] = {
         "workload": "24576 x 7168 fp8 receive buffer, group-128 fp32 scales, "
-                    "first 8192 rows upscaled to bf16",
-        "us": round(us, 2), "algorithmic_bytes": byts,
-        "gbs": round(byts / (us * 1e-6) / 1e9, 2),
+                    "first 8192 rows upscaled to bf16", **up,
         "rotating_outputs_us": round(us_rot, 2),
         "rotating_outputs_gbs": round(byts / (us_rot * 1e-6) / 1e9, 2)}
     del qu, su, ou, ous
@@ -883,12 +1065,10 @@ def other_rows(torch, mxq, si, dev):
             (B_, N_ // 128, K_ // 128), 2.0 ** -16, 2.0 ** -8)).to(dev)
         qo = torch.empty_like(qw)
         so = torch.empty(sw.shape, dtype=torch.uint8, device=dev)
-        us = time_calls(torch, lambda: mxq.requant_weight_block_ue8m0(
-            qw, sw, q_out=qo, scales_out=so), reps=10)
         nblk = B_ * (N_ // 128) * (K_ // 128)
-        byts = 2 * qw.numel() + 5 * nblk
-        wr[name] = {"us": round(us, 2), "algorithmic_bytes": byts,
-                    "gbs": round(byts / (us * 1e-6) / 1e9, 2)}
+        wr[name] = timed_row(torch, lambda: mxq.requant_weight_block_ue8m0(
+            qw, sw, q_out=qo, scales_out=so), nbytes=2 * qw.numel() + 5 * nblk,
+            reps=10)
         del qw, sw, qo, so
     rows["weight_requant"] = wr
 
@@ -899,18 +1079,22 @@ def other_rows(torch, mxq, si, dev):
     yl = si.gaussian_bf16_device(505, (lay["num_rows"], 4096), dev)
     wd = torch.from_numpy(cw).to(dev)
     ol = torch.empty((16384, 4096), dtype=torch.bfloat16, device=dev)
-    us = time_calls(torch, lambda: mxq.moe_combine(yl, lay["src2dst"], wd,
-                                                   out=ol))
-    us_cold = time_calls_cold(torch, lambda: mxq.moe_combine(
-        yl, lay["src2dst"], wd, out=ol), flush)
     byts = bytes_combine(16384, 8, 4096, 16384 * 8)
-    rows["large_combine"] = {"workload": "T=16384, hidden 4096, 128 experts "
-                                         "top-8, 147328-row layout",
-                             "us": round(us, 2), "algorithmic_bytes": byts,
-                             "gbs": round(byts / (us * 1e-6) / 1e9, 2),
-                             "cold_us": round(us_cold, 2),
-                             "cold_gbs": round(byts / (us_cold * 1e-6) / 1e9,
-                                               2)}
+    rows["large_combine"] = {
+        "workload": "T=16384, hidden 4096, 128 experts top-8, 147328-row "
+                    "layout",
+        **timed_row(torch, lambda: mxq.moe_combine(yl, lay["src2dst"], wd,
+                                                   out=ol),
+                    nbytes=byts, flush=flush)}
+    if cpu:
+        yl_h = yl.view(torch.int16).cpu().numpy().view(np.uint16)
+        s2d_h = lay["src2dst"].cpu().numpy()
+        rows["large_combine"]["cpu_baseline"] = cpu_row(
+            lambda: oracle.combine(yl_h, s2d_h, cw), nbytes=byts,
+            units=16384, unit_name="tokens")
+        rows["large_combine"]["cpu_baseline"]["sample"] = (
+            "the whole combine (131072 rows -> 16384 tokens)")
+        del yl_h
     del flush
     return rows
 
