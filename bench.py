@@ -56,6 +56,11 @@ def parse_args():
     p.add_argument("--no-rows", action="store_true",
                    help="skip the separately timed rows")
     p.add_argument("--cpu-repeats", type=int, default=3)
+    p.add_argument("--samples", type=int, default=100,
+                   help="samples behind each median and spread: steps of "
+                        "the per-kernel and MALL-flushed passes, graph "
+                        "replays and flushed calls of every row (fewer for "
+                        "runs under a profiler)")
     p.add_argument("--sweep", action="store_true",
                    help="instead of the step, time masked against compact "
                         "layouts over a range of token counts")
@@ -115,8 +120,9 @@ def time_calls_samples(torch, fn, reps=20, warmup=3, replays=100):
     return per
 
 
-def time_calls(torch, fn, reps=20, warmup=3, replays=100):
+def time_calls(torch, fn, reps=20, warmup=3, replays=None):
     """Median of time_calls_samples."""
+    replays = SAMPLES if replays is None else replays
     return float(np.median(time_calls_samples(torch, fn, reps, warmup,
                                               replays)))
 
@@ -150,11 +156,15 @@ def time_calls_cold(torch, fn, flush, reps=100, warmup=2):
                                                    warmup)))
 
 
+SAMPLES = 100  # set from --samples in main()
+
+
 def timed_row(torch, fn, nbytes=None, units=None, unit_name=None, reps=20,
-              replays=100, flush=None):
+              replays=None, flush=None):
     """A row's record: median time per call with its 10-90 % spread over
     `replays` graph replays (and over as many calls with the MALL flushed
     when `flush` is given), plus GB/s of `nbytes` and `unit_name`/s."""
+    replays = SAMPLES if replays is None else replays
     per = time_calls_samples(torch, fn, reps=reps, replays=replays)
     us = float(np.median(per))
     r = {"us": round(us, 2), "us_spread": spread(per)}
@@ -164,7 +174,7 @@ def timed_row(torch, fn, nbytes=None, units=None, unit_name=None, reps=20,
     if units is not None:
         r[unit_name + "_per_s"] = round(units / (us * 1e-6), 1)
     if flush is not None:
-        cold = time_calls_cold_samples(torch, fn, flush)
+        cold = time_calls_cold_samples(torch, fn, flush, reps=replays)
         cu = float(np.median(cold))
         r["cold_us"] = round(cu, 2)
         r["cold_us_spread"] = spread(cold)
@@ -288,6 +298,9 @@ def main():
     import fp8_mx_activation_amd as mxq
     import synthetic_inputs as si
 
+    global SAMPLES
+    SAMPLES = max(1, args.samples)
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -405,7 +418,7 @@ def main():
 
     # per-kernel pass: the same steps with events around each kernel, at
     # least 100 of them whatever --steps is, for the spread of each kernel
-    n_k = max(args.steps, 100)
+    n_k = max(args.steps, args.samples)
     kev = HipEvents(4 * n_k)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -439,7 +452,7 @@ def main():
     # cache); events bracket the step's kernels alone.  100 steps.
     flush = torch.zeros(512 << 20, dtype=torch.uint8,
                         device=dev).view(torch.float32)
-    n_cold = 100
+    n_cold = args.samples
     evc = HipEvents(4 * n_cold)
     torch.cuda.synchronize()
     for i in range(n_cold):
@@ -464,16 +477,20 @@ def main():
     # time the combine would take if its reads and writes simply added up.
     gather_sink = torch.empty(T, dtype=torch.int32, device=dev)
     s2d = lay_out["src2dst"]
+    ns = args.samples
     gather_us = time_calls_samples(
-        torch, lambda: mxq.mxq_gather_read16(y, s2d, gather_sink))
-    write_us = time_calls_samples(torch, lambda: mxq.mxq_fill_rows16(out))
+        torch, lambda: mxq.mxq_gather_read16(y, s2d, gather_sink),
+        replays=ns)
+    write_us = time_calls_samples(torch, lambda: mxq.mxq_fill_rows16(out),
+                                  replays=ns)
     comb_us_graph = time_calls_samples(
-        torch, lambda: mxq.moe_combine(y, s2d, w, out=out))
+        torch, lambda: mxq.moe_combine(y, s2d, w, out=out), replays=ns)
     # the same three with the MALL flushed before each call
     gather_cold = time_calls_cold_samples(
-        torch, lambda: mxq.mxq_gather_read16(y, s2d, gather_sink), flush)
+        torch, lambda: mxq.mxq_gather_read16(y, s2d, gather_sink), flush,
+        reps=ns)
     write_cold = time_calls_cold_samples(
-        torch, lambda: mxq.mxq_fill_rows16(out), flush)
+        torch, lambda: mxq.mxq_fill_rows16(out), flush, reps=ns)
     del flush
 
     value = B_step / (step_ms * 1e-3) / 1e9
