@@ -7,8 +7,10 @@
 // slots with masked_m, overflow fails fast).  Slots inside an expert follow
 // ascending flat assignment index t*K + j.
 //
-// Two launches whose grids depend only on T*K, E and num_rows (one launch,
-// the assign kernel in its SINGLE form, when T*K <= 4096):
+// Two launches whose grids depend only on T*K, E and num_rows; one launch,
+// the assign kernel alone, when T*K <= 4096 (every block ranks the whole
+// routing) or when T*K <= 2^14 with at most 256 experts (every block counts
+// the whole routing into LDS in place of the histogram launch):
 //   layout_hist_kernel    one block per chunk of assignments: LDS histogram
 //                         of the chunk's local experts -> cnt[chunk][E].
 //   layout_assign_kernel  one block of 16 wavefronts per chunk, plus enough
@@ -78,11 +80,18 @@ __global__ __launch_bounds__(256) void layout_hist_kernel(
 // chunk base + count of the same expert in earlier wavefronts + its rank in
 // its wavefront: flat order, no atomics, no serial chain across wavefronts.
 //
-// SINGLE: all assignments form one chunk (T*K <= kSingleMax) and no
+// MODE kFromChunks: the totals and this chunk's first slots come from the
+// histogram launch's per-chunk counts.
+// MODE kSingle: all assignments form one chunk (T*K <= kSingleMax) and no
 // histogram pass runs.  Every block ranks that chunk (C1), takes the totals
 // from the per-wavefront counts (C2) and then scans the regions (B); block 0
 // alone writes src2dst.
-template <bool SINGLE>
+// MODE kInBlock: no histogram launch either; every block counts the whole
+// routing itself (A'), wavefront w adding each local id of its share to its
+// private LDS count of ids before the block's chunk or from it on.
+enum AssignMode { kFromChunks = 0, kSingle = 1, kInBlock = 2 };
+
+template <int MODE>
 __global__ __launch_bounds__(1024) void layout_assign_kernel(
     const int32_t* __restrict__ ids, int64_t A, int32_t begin, int32_t E,
     int32_t nbits, int32_t kind, int32_t block_e, int32_t cap,
@@ -106,6 +115,7 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
+  constexpr bool SINGLE = MODE == kSingle;
   const int c = SINGLE ? 0 : (int)blockIdx.x;
   const bool has_chunk = c < nc;
   const bool writer = SINGLE ? blockIdx.x == 0 : has_chunk;
@@ -129,10 +139,55 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
     for (int st = 0; st < kMaxStepsPerWave; ++st) idb[st] = 0;
   }
 
+  // A': totals and this chunk's first slots counted here.  Wavefront w takes
+  // a contiguous share of the ids, 64 * kScanBatch at a time (indices
+  // clamped so that a batch's loads are in flight together), and adds each
+  // local one to its private count: hist[0][w] for ids before this block's
+  // chunk, hist[1][w] for the others.  The counts live in the row-table
+  // space, which is only used in phase D (the host checks that 2 * 16 * E
+  // entries fit).
+  if constexpr (MODE == kInBlock) {
+    int32_t* hist = tbl;  // [2][kAssignWaves][E]
+    for (int i = tid; i < 2 * kAssignWaves * E; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    const int64_t per = (A + 64 * kAssignWaves - 1) / (64 * kAssignWaves) * 64;
+    const int64_t a0 = (int64_t)wv * per;
+    const int64_t a1 = min(A, a0 + per);
+    int32_t* h_lo = hist + wv * E;
+    int32_t* h_hi = hist + (kAssignWaves + wv) * E;
+    for (int64_t ab = a0; ab < a1; ab += 64 * kScanBatch) {
+      int32_t v[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u)
+        v[u] = ids[min(ab + u * 64 + lane, a1 - 1)];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        const int64_t a = ab + u * 64 + lane;
+        const int64_t e = (int64_t)v[u] - begin;
+        if (a < a1 && e >= 0 && e < E)
+          atomicAdd((a < c_begin ? h_lo : h_hi) + e, 1);
+      }
+    }
+    __syncthreads();
+    int total = 0, first = 0;
+    if (tid < E) {
+#pragma unroll 4
+      for (int w = 0; w < kAssignWaves; ++w) {
+        const int lo = hist[w * E + tid];
+        total += lo + hist[(kAssignWaves + w) * E + tid];
+        first += lo;
+      }
+      tot[tid] = total;
+      cbase[tid] = first;
+    }
+    region_scan(total, E, kind, block_e, cap, off, wsum, counts, offsets,
+                masked_m, overflow);
+  }
+
   // A: totals and this chunk's first slots from the chunk counts.  Up to
   // four groups of threads per expert split the chunks; each issues its
   // loads a batch at a time.
-  if constexpr (!SINGLE) {
+  if constexpr (MODE == kFromChunks) {
     const int er = (E + 63) / 64 * 64;
     const int nparts = max(1, (int)blockDim.x / er);
     const int part = tid / er;
@@ -352,7 +407,12 @@ mxq_status layout_launch(const int32_t* topk_ids, int64_t T, int32_t K,
   hipStream_t s = as_stream(stream);
   const int32_t cap = kind == MXQ_LAYOUT_MASKED ? capacity : 0;
   const bool single = A <= kSingleMax;
-  if (g.nc > 0 && !single) {
+  const size_t fixed = (size_t)(3 * E + 1) * sizeof(int32_t) +
+                       (size_t)kAssignWaves * E * sizeof(uint16_t);
+  const int32_t tbl_cap = (int32_t)((kAssignLds - fixed) / sizeof(int32_t));
+  const bool in_block = layout_in_block(A, E);
+  if (in_block && tbl_cap < 2 * kAssignWaves * E) return MXQ_ERR_UNSUPPORTED;
+  if (g.nc > 0 && !single && !in_block) {
     layout_hist_kernel<<<g.nc, 256, (size_t)E * sizeof(int32_t), s>>>(
         topk_ids, A, expert_begin, E, g.chunk, chunk_cnt);
     if (launch_status() != MXQ_OK) return MXQ_ERR_HIP;
@@ -373,16 +433,19 @@ mxq_status layout_launch(const int32_t* topk_ids, int64_t T, int32_t K,
     if (fill_blocks > 64) fill_blocks = 64;
     if (fill_blocks > blocks) blocks = fill_blocks;
   }
-  const size_t fixed = (size_t)(3 * E + 1) * sizeof(int32_t) +
-                       (size_t)kAssignWaves * E * sizeof(uint16_t);
-  const int32_t tbl_cap = (int32_t)((kAssignLds - fixed) / sizeof(int32_t));
   if (single)
-    layout_assign_kernel<true><<<(unsigned)blocks, 1024, kAssignLds, s>>>(
+    layout_assign_kernel<kSingle><<<(unsigned)blocks, 1024, kAssignLds, s>>>(
+        topk_ids, A, expert_begin, E, nbits, (int32_t)kind, block_e, cap,
+        num_rows, chunk, nc, steps_per_wave, tbl_cap, nullptr, counts,
+        expert_offsets, masked_m, overflow_flag, m_indices, src2dst);
+  else if (in_block)
+    layout_assign_kernel<kInBlock><<<(unsigned)blocks, 1024, kAssignLds, s>>>(
         topk_ids, A, expert_begin, E, nbits, (int32_t)kind, block_e, cap,
         num_rows, chunk, nc, steps_per_wave, tbl_cap, nullptr, counts,
         expert_offsets, masked_m, overflow_flag, m_indices, src2dst);
   else
-    layout_assign_kernel<false><<<(unsigned)blocks, 1024, kAssignLds, s>>>(
+    layout_assign_kernel<kFromChunks><<<(unsigned)blocks, 1024, kAssignLds,
+                                        s>>>(
         topk_ids, A, expert_begin, E, nbits, (int32_t)kind, block_e, cap,
         num_rows, chunk, nc, steps_per_wave, tbl_cap, chunk_cnt, counts,
         expert_offsets, masked_m, overflow_flag, m_indices, src2dst);

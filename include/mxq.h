@@ -102,8 +102,10 @@ int64_t moe_compact_row_bound(int64_t num_assignments,
  * num_local_experts <= 32, else 0 (compact).  Pure host function. */
 int32_t moe_should_use_masked(int32_t num_experts, int32_t num_local_experts);
 
-/* Workspace bytes moe_layout needs for T tokens, top-K, E local experts (0
- * when T*K <= 4096: one launch then handles the whole routing). */
+/* Workspace bytes moe_layout needs for T tokens, top-K, E local experts: 0
+ * when T*K <= 4096, or T*K <= 2^14 with E <= 256 (the layout then runs as
+ * one launch that counts the whole routing in every block), else the
+ * per-chunk expert counts of its histogram launch. */
 size_t moe_layout_workspace_bytes(int64_t T, int32_t K, int32_t E);
 
 /* Workspace bytes requant_per_token_to_per_tensor needs. */
@@ -165,9 +167,9 @@ mxq_status moe_read_overflow(const int32_t* overflow_flag, int32_t* host_value,
  * workspace live instead in a static device array of the library,
  * MXQ_LAYOUT_NOALLOC_SCRATCH_BYTES per device, held until the process ends.
  * A routing whose moe_layout_workspace_bytes(T, K, E) exceeds that returns
- * MXQ_ERR_SCRATCH_LIMIT and enqueues nothing (the prefill routing of 8192
- * tokens, top-8 over 256 experts needs 64 KiB; none is needed when
- * T*K <= 4096).  The call allocates nothing.  Its first call on a device
+ * MXQ_ERR_SCRATCH_LIMIT and enqueues nothing (8192 tokens, top-8 over 384
+ * experts need 96 KiB; routings for which moe_layout needs no workspace use
+ * none of it).  The call allocates nothing.  Its first call on a device
  * looks up that device's copy of the array (a host query, no allocation);
  * make it outside graph capture.  Every call on one device shares the array:
  * calls that overlap on one device (e.g. on two streams) race and must be

@@ -69,7 +69,12 @@ def test_host_helpers_match_oracle(mxq, ora):
 def test_workspace_sizes(mxq):
     assert mxq.moe_layout_workspace_bytes(0, 8, 256) == 0
     assert mxq.moe_layout_workspace_bytes(512, 8, 256) == 0    # one launch
-    assert mxq.moe_layout_workspace_bytes(513, 8, 256) > 0
+    # up to 2^14 assignments over at most 256 experts every block of the
+    # slot kernel counts the routing itself: no workspace either
+    assert mxq.moe_layout_workspace_bytes(513, 8, 256) == 0
+    assert mxq.moe_layout_workspace_bytes(2048, 8, 256) == 0
+    assert mxq.moe_layout_workspace_bytes(513, 8, 257) > 0
+    assert mxq.moe_layout_workspace_bytes(2049, 8, 256) > 0
     w = mxq.moe_layout_workspace_bytes(8192, 8, 256)
     assert 0 < w <= 64 * 256 * 4
     assert mxq.requant_workspace_bytes(16384, 4096) >= 4
@@ -288,9 +293,11 @@ def test_layout_validation(mxq):
     assert call(kind=5) == UNSUPPORTED
     assert call(kind=1, cap=0, rows=0) == INVALID
     assert call(kind=1, cap=16, rows=63) == INVALID  # E * cap = 64
-    # T*K above 4096 needs the per-chunk count workspace
-    assert call(T=2048, K=8, ws=None) == WORKSPACE
-    assert call(T=2048, K=8, wsb=4) == WORKSPACE
+    # the per-chunk count workspace: needed above 4096 assignments with more
+    # than 256 experts, or above 2^14 assignments
+    assert call(T=2048, K=8, E=300, ws=None) == WORKSPACE
+    assert call(T=2048, K=8, E=300, wsb=4) == WORKSPACE
+    assert call(T=20000, K=8, ws=None) == WORKSPACE
     assert call(ids=None) == INVALID
     assert call(block=0, rows=1024) == INVALID
     assert call(T=(1 << 21) + 1, K=8, rows=1 << 30) == UNSUPPORTED  # > 2^24
@@ -319,8 +326,9 @@ def test_layout_noalloc_validation(mxq):
     assert call(T=1 << 21, K=8, E=1024) == SCRATCH
     assert mxq.MXQ_ERR_SCRATCH_LIMIT == SCRATCH
     assert b"scratch" in L.mxq_status_string(SCRATCH)
-    # the prefill routing (8192 x top-8 over 256 experts) fits: 64 KiB
-    assert mxq.moe_layout_workspace_bytes(8192, 8, 256) <= \
+    # a prefill-sized routing that uses the counts (8192 x top-8 over 384
+    # experts) fits: 96 KiB
+    assert 0 < mxq.moe_layout_workspace_bytes(8192, 8, 384) <= \
         mxq.LAYOUT_NOALLOC_SCRATCH_BYTES
 
 

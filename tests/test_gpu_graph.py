@@ -142,11 +142,26 @@ def test_graph_replay_full_path(ora):
 
 
 def test_graph_replay_variants_upscale_weights(ora):
-    """The scale variants, the upscale, the weight requant and a two-launch
-    layout (T*K > 8192) captured once and replayed three times with new
-    inputs and eager work between replays; every replay is checked."""
+    """The scale variants, the upscale, the weight requant and the layout in
+    both of its launch forms above 4096 assignments (8800 over 40 experts:
+    one launch that counts the routing in every block; the same ids over
+    300 experts: histogram launch + slot launch with the per-chunk
+    workspace) captured once and replayed three times with new inputs and
+    eager work between replays; every replay is checked."""
     T, H, E, K, G = 1100, 256, 40, 8, 32
     R = ora.compact_row_bound(T * K, E, 128)
+    E2 = 300
+    R2 = ora.compact_row_bound(T * K, E2, 128)
+    lay_out2 = {k: torch.empty(shape, dtype=torch.int32, device=DEV)
+                for k, shape in (("counts", (E2,)),
+                                 ("expert_offsets", (E2 + 1,)),
+                                 ("m_indices", (R2,)), ("masked_m", (E2,)),
+                                 ("src2dst", (T, K)),
+                                 ("overflow_flag", (1,)))}
+    assert mxq.moe_layout_workspace_bytes(T, K, E) == 0
+    assert mxq.moe_layout_workspace_bytes(T, K, E2) > 0
+    ws2 = torch.empty(mxq.moe_layout_workspace_bytes(T, K, E2),
+                      dtype=torch.uint8, device=DEV)
     ng = H // G
     ids_s = torch.zeros((T, K), dtype=torch.int32, device=DEV)
     x_s = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
@@ -172,6 +187,8 @@ def test_graph_replay_variants_upscale_weights(ora):
     def step():
         lay = mxq.moe_layout(ids_s, 0, E, "compact", num_rows=R, out=lay_out,
                              workspace=ws)
+        mxq.moe_layout(ids_s, 0, E2, "compact", num_rows=R2, out=lay_out2,
+                       workspace=ws2)
         mxq.moe_scatter_quant_ex(x_s, lay["src2dst"], R, "e8m0_g32",
                                  "ocp_floor", "packed_mn", q=q_s,
                                  scales=pk_s)
@@ -223,6 +240,13 @@ def test_graph_replay_variants_upscale_weights(ora):
 
         ref = ora.moe_layout(ids, 0, E, "compact", num_rows=R)
         assert_equal(host(lay_out["src2dst"]), ref["src2dst"], "src2dst")
+        assert_equal(host(lay_out["m_indices"]), ref["m_indices"],
+                     "m_indices")
+        ref2 = ora.moe_layout(ids, 0, E2, "compact", num_rows=R2)
+        assert_equal(host(lay_out2["src2dst"]), ref2["src2dst"],
+                     "src2dst (two launches)")
+        assert_equal(host(lay_out2["m_indices"]), ref2["m_indices"],
+                     "m_indices (two launches)")
         q_ref, pk_ref = ora.scatter_quant_ex(
             x, ref["src2dst"], G, R, "ocp_floor", "packed_mn",
             q=np.full((R, H), 0xA5, np.uint8),

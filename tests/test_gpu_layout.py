@@ -116,16 +116,38 @@ def test_empty_batch(ora):
                                    (129, 8, 256), (4096, 1, 7), (4097, 1, 7),
                                    (128, 8, 32)])
 def test_single_launch_boundary(ora, T, K, E):
-    """Around T*K = 4096, where one launch (every block ranking the whole
-    routing) gives way to the histogram + slots pair: 4096, 4092, 1032 and
-    1024 take the single launch, 4104 and 4097 the pair; masked capacity
-    small enough to overflow."""
+    """Around T*K = 4096, where one launch with every block ranking the
+    whole routing gives way to the slot kernel over chunks: 4096, 4092, 1032
+    and 1024 take the single launch; 4104 (1024 experts) and 4104 (300
+    experts) the histogram + slots pair, 4097 over 7 experts the slot kernel
+    counting the routing in every block; masked capacity small enough to
+    overflow."""
     rng = np.random.default_rng(T * K + E)
     ids = si.zipf_topk(rng, T, E, K) if E >= 2 * K else si.uniform_topk(
         rng, T, E, K)
     run_both(ora, ids, 0, E, "compact")
     run_both(ora, ids, 0, E, "compact", block_e=1)
     got, ref = run_both(ora, ids, 0, E, "masked", cap=max(1, T * K // E // 2))
+
+
+@pytest.mark.parametrize("T,K,E", [(4097, 1, 256), (4097, 1, 257),
+                                   (2048, 8, 256), (2049, 8, 256),
+                                   (2048, 8, 128), (1024, 8, 32),
+                                   (8192, 2, 1), (1024, 8, 300)])
+def test_counted_in_block_boundary(ora, T, K, E):
+    """Where every block of the slot kernel counts the whole routing itself
+    (4096 < T*K <= 2^14, at most 256 experts) against where the histogram
+    launch counts it: 4097 and 16384 assignments over 256 experts, 16384
+    over 128 and 1 and 8192 over 32 take the in-block count; 257 and 300
+    experts and 16392 assignments the histogram; compact, one-row blocks
+    and masked (with overflow) for each.  An expert window puts part of the
+    ids out of range."""
+    rng = np.random.default_rng(T * K + E + 7)
+    ids = si.zipf_topk(rng, T, E + 16, K, n_zero=4) if E + 16 >= 2 * K \
+        else si.uniform_topk(rng, T, E + 16, K)
+    run_both(ora, ids, 8, E, "compact")
+    run_both(ora, ids, 8, E, "compact", block_e=1)
+    run_both(ora, ids, 8, E, "masked", cap=max(1, T * K // E // 2))
 
 
 def test_many_assignments(ora):

@@ -54,11 +54,13 @@ def call_with_workspace(mxq, ids, E, kind, block_e, cap, rows, o):
 
 
 CASES = (
-    # (name, T, K, E, kind, cap): first a prefill-sized routing, then a
-    # smaller one that uses fewer chunks of the shared array
-    ("prefill-zipf", 8192, 8, 256, "compact", 0),
-    ("smaller-zipf", 1500, 8, 256, "compact", 0),
-    ("masked-after", 2048, 8, 32, "masked", 1024),
+    # (name, T, K, E, kind, cap): routings whose per-chunk counts go through
+    # the shared array (more than 256 experts, or more than 2^17
+    # assignments): first a prefill-sized one, then a smaller one that uses
+    # fewer chunks of it, then a masked one
+    ("prefill-zipf", 8192, 8, 384, "compact", 0),
+    ("smaller-zipf", 1500, 8, 384, "compact", 0),
+    ("masked-after", 20000, 8, 32, "masked", 1024),
 )
 
 
