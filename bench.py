@@ -979,18 +979,30 @@ def other_rows(torch, mxq, si, dev, cpu=True):
     sc_eq = torch.full_like(sc, 2.0 ** -3)
     rq_eq = timed_row(torch, lambda: mxq.requant_per_token_to_per_tensor(
         qi, sc_eq, q_out=qo, tensor_scale=Sd, workspace=rws), nbytes=byts)
+    # the max pass's worst case: equal scales and no row holding +-448 (the
+    # 448 bytes lowered to 416), so no row attains the common bound and
+    # every row must be read
+    qi_low = torch.where((qi & 0x7F) == 0x7E, qi - 1, qi)
+    rq_wc = timed_row(torch, lambda: mxq.requant_per_token_to_per_tensor(
+        qi_low, sc_eq, q_out=qo, tensor_scale=Sd, workspace=rws),
+        nbytes=byts)
+    del qi_low
     rows["requant"] = {"workload": "16384 x 4096 fp8, per-token scales "
                                    "2^U, U~U[-8,4]", **rq,
                        "equal_scales_us": rq_eq["us"],
                        "equal_scales_gbs": rq_eq["gbs"],
                        "equal_scales_us_spread": rq_eq["us_spread"],
+                       "equal_scales_no_row_at_448_us": rq_wc["us"],
+                       "equal_scales_no_row_at_448_gbs": rq_wc["gbs"],
                        "note": "warm: the 64 MiB input stays in the 256 MB "
                                "MALL across the two passes and back-to-back "
                                "calls; cold: MALL flushed by reading 512 MB "
                                "before each call; equal_scales: every token "
                                "scale 2^-3, so every row's bound is the "
                                "largest (rows holding 448 settle the max "
-                               "pass at once) (warm)"}
+                               "pass at once) (warm); equal_scales_no_row_"
+                               "at_448: the same with no byte at +-448, so "
+                               "the max pass reads every row (warm)"}
     if cpu:
         rows["requant"]["cpu_baseline"] = cpu_row(
             lambda: oracle.requant_per_token_to_per_tensor(rb.q, rb.scales),
