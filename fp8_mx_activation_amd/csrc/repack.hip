@@ -18,8 +18,9 @@
 // The copies of large slabs launch blocks per (expert, range of slab rows);
 // a block deals its rows' 16-byte vectors to its threads and issues a round
 // of loads before the stores.  Small slabs with at most 64 experts use a
-// fixed grid that deals (real row, chunk) units to wavefronts instead.  All grids depend only on host arguments, so every call
-// can be captured in a hipGraph.
+// fixed grid that deals (real row, chunk) units to wavefronts instead.  All
+// grids depend only on host arguments, so every call can be captured in a
+// hipGraph.
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
 
