@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import sys
@@ -127,27 +128,42 @@ def time_calls(torch, fn, reps=20, warmup=3, replays=None):
                                               replays)))
 
 
-def time_calls_cold_samples(torch, fn, flush, reps=100, warmup=2):
+def time_calls_cold_wb(torch, fn, flush, reps=100, warmup=2):
     """GPU time per call of fn with the 256 MB last-level cache (MALL) and
     the L2s flushed before each call by reading `flush` (512 MB, written
     once beforehand, so the evicting lines are clean and nothing is written
-    back during the call): events bracket the call alone; one sample per
-    call, in microseconds."""
+    back during the call); events bracket the call alone.  Lines the call
+    leaves dirty in the MALL reach HBM only later, so a flush right after
+    the call is timed against a flush after a flush, and the median of that
+    difference (the write-back, at least 0) is added to every sample.
+    Returns (samples in microseconds, write-back in microseconds)."""
     for _ in range(warmup):
         fn()
     flush_f = flush.view(torch.float32)
     torch.cuda.synchronize()
     hs = torch.cuda.current_stream().cuda_stream
-    ev = HipEvents(2 * reps)
+    ev = HipEvents(4 * reps)
     for i in range(reps):
         flush_f.sum()
-        ev.record(2 * i, hs)
+        ev.record(4 * i, hs)
         fn()
-        ev.record(2 * i + 1, hs)
+        ev.record(4 * i + 1, hs)
+        flush_f.sum()
+        ev.record(4 * i + 2, hs)
+        flush_f.sum()
+        ev.record(4 * i + 3, hs)
     torch.cuda.synchronize()
-    per = [ev.ms(2 * i, 2 * i + 1) * 1e3 for i in range(reps)]
+    per = [ev.ms(4 * i, 4 * i + 1) * 1e3 for i in range(reps)]
+    wb = max(0.0, float(np.median(
+        [(ev.ms(4 * i + 1, 4 * i + 2) - ev.ms(4 * i + 2, 4 * i + 3)) * 1e3
+         for i in range(reps)])))
     ev.close()
-    return per
+    return [p + wb for p in per], wb
+
+
+def time_calls_cold_samples(torch, fn, flush, reps=100, warmup=2):
+    """The samples of time_calls_cold_wb (write-back included)."""
+    return time_calls_cold_wb(torch, fn, flush, reps, warmup)[0]
 
 
 def time_calls_cold(torch, fn, flush, reps=100, warmup=2):
@@ -157,6 +173,15 @@ def time_calls_cold(torch, fn, flush, reps=100, warmup=2):
 
 
 SAMPLES = 100  # set from --samples in main()
+
+# output buffers a combine timing rotates over (see the step's setup)
+N_OUT = 4
+
+
+def rotation(bufs):
+    """A function returning bufs[0], bufs[1], ... in turn, cyclically."""
+    it = itertools.cycle(bufs)
+    return lambda: next(it)
 
 
 def timed_row(torch, fn, nbytes=None, units=None, unit_name=None, reps=20,
@@ -174,10 +199,11 @@ def timed_row(torch, fn, nbytes=None, units=None, unit_name=None, reps=20,
     if units is not None:
         r[unit_name + "_per_s"] = round(units / (us * 1e-6), 1)
     if flush is not None:
-        cold = time_calls_cold_samples(torch, fn, flush, reps=replays)
+        cold, wb = time_calls_cold_wb(torch, fn, flush, reps=replays)
         cu = float(np.median(cold))
         r["cold_us"] = round(cu, 2)
         r["cold_us_spread"] = spread(cold)
+        r["cold_write_back_us"] = round(wb, 2)
         if nbytes is not None:
             r["cold_gbs"] = round(nbytes / (cu * 1e-6) / 1e9, 2)
     return r
@@ -241,25 +267,29 @@ class HipEvents:
         self.ev = []
 
 
-def graph_step_ms(torch, fn, warmup, steps):
-    """Capture fn once in a hipGraph; time `steps` replays."""
+def graph_step_ms(torch, fn, warmup, steps, per_graph=1):
+    """Capture fn(0), ..., fn(per_graph - 1) once in a hipGraph; time
+    replays covering `steps` steps; milliseconds per step."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        fn()
+        for i in range(per_graph):
+            fn(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        fn()
-    for _ in range(warmup):
+        for i in range(per_graph):
+            fn(i)
+    n = max(1, steps // per_graph)
+    for _ in range(max(1, warmup // per_graph)):
         g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for _ in range(n):
         g.replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    return (time.perf_counter() - t0) * 1e3 / (n * per_graph)
 
 
 def traffic_record():
@@ -324,7 +354,14 @@ def main():
                      dtype=torch.uint8, device=dev)
     q = torch.empty((R, H), dtype=torch.uint8, device=dev)
     s = torch.empty((R, H // G), dtype=torch.uint8, device=dev)
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    # The combine's output rotates over N_OUT buffers (470 MB, more than the
+    # 256 MB MALL) in every warm timing: its device-scope stores leave lines
+    # dirty in the MALL, and one buffer rewritten every step could be
+    # overwritten there without ever reaching HBM.  With four, a buffer's
+    # lines are written back before the step that writes it again.
+    outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            for _ in range(N_OUT)]
+    out = outs[0]
 
     local = ((b.topk_ids >= 0) & (b.topk_ids < E))
     A = int(local.sum())
@@ -348,12 +385,12 @@ def main():
         copy16[name] = round(2 * cbuf_a.numel() / (us * 1e-6) / 1e9, 1)
     del cbuf_a, cbuf_b
 
-    def step():
+    def step(i=0):
         lay = mxq.moe_layout(ids, 0, E, "compact", num_rows=R, out=lay_out,
                              workspace=ws)
         mxq.moe_scatter_quant(x, lay["src2dst"], R, "ue8m0_g128", q=q,
                               scales=s)
-        mxq.moe_combine(y, lay["src2dst"], w, out=out)
+        mxq.moe_combine(y, lay["src2dst"], w, out=outs[i % N_OUT])
 
     # The timed loop calls the C entry points directly with arguments
     # prepared once (the same calls the wrappers above make), and its events
@@ -369,8 +406,9 @@ def main():
     sq_args = (x.data_ptr(), H, T, H, p["src2dst"], K,
                mxq.SCALE_FORMATS["ue8m0_g128"][0], q.data_ptr(), H,
                s.data_ptr(), H // G, R, hs)
-    cb_args = (y.data_ptr(), H, R, p["src2dst"], w.data_ptr(), T, K, H,
-               out.data_ptr(), H, mxq.OUT_DTYPES[torch.bfloat16], hs)
+    cb_argv = [(y.data_ptr(), H, R, p["src2dst"], w.data_ptr(), T, K, H,
+                o.data_ptr(), H, mxq.OUT_DTYPES[torch.bfloat16], hs)
+               for o in outs]
     # Timing events are HIP events on the launch stream with the system
     # fence disabled (HipEvents).  The timed region holds one pair per step,
     # around the combine (the roofline kernel); the layout and scatter times
@@ -382,12 +420,12 @@ def main():
         st = L.moe_layout(*lay_args)
         st |= L.moe_scatter_quant(*sq_args)
         st |= hev.record(2 * i, hs)
-        st |= L.moe_combine(*cb_args)
+        st |= L.moe_combine(*cb_argv[i % N_OUT])
         st |= hev.record(2 * i + 1, hs)
         return st
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     status = 0
     t0 = time.perf_counter()
@@ -410,7 +448,7 @@ def main():
     for i in range(args.steps):
         status |= L.moe_layout(*lay_args)
         status |= L.moe_scatter_quant(*sq_args)
-        status |= L.moe_combine(*cb_args)
+        status |= L.moe_combine(*cb_argv[i % N_OUT])
     torch.cuda.synchronize()
     noev_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     if status != 0:
@@ -428,7 +466,7 @@ def main():
         status |= kev.record(4 * i + 1, hs)
         status |= L.moe_scatter_quant(*sq_args)
         status |= kev.record(4 * i + 2, hs)
-        status |= L.moe_combine(*cb_args)
+        status |= L.moe_combine(*cb_argv[i % N_OUT])
         status |= kev.record(4 * i + 3, hs)
     torch.cuda.synchronize()
     kev_step_ms = (time.perf_counter() - t0) * 1e3 / n_k
@@ -443,7 +481,7 @@ def main():
 
     # the same step captured once in a hipGraph and replayed (no per-kernel
     # host launch cost); reported beside the eager timed region
-    graph_ms = graph_step_ms(torch, step, args.warmup, args.steps)
+    graph_ms = graph_step_ms(torch, step, args.warmup, args.steps, N_OUT)
 
     # The same step with the 256 MB last-level cache (MALL) and the L2s
     # flushed before each step by reading 512 MB, so that every input comes
@@ -465,7 +503,7 @@ def main():
         status |= evc.record(6 * i + 1, hs)
         status |= L.moe_scatter_quant(*sq_args)
         status |= evc.record(6 * i + 2, hs)
-        status |= L.moe_combine(*cb_args)
+        status |= L.moe_combine(*cb_argv[i % N_OUT])
         status |= evc.record(6 * i + 3, hs)
         flush.sum()
         status |= evc.record(6 * i + 4, hs)
@@ -485,22 +523,24 @@ def main():
     # same 65536 rows through the same src2dst, non-temporal loads) and its
     # 117 MB of output rows written with streaming stores; their sum is the
     # time the combine would take if its reads and writes simply added up.
+    # Successive calls write the rotating output buffers in turn.
     gather_sink = torch.empty(T, dtype=torch.int32, device=dev)
     s2d = lay_out["src2dst"]
     ns = args.samples
     gather_us = time_calls_samples(
         torch, lambda: mxq.mxq_gather_read16(y, s2d, gather_sink),
         replays=ns)
-    write_us = time_calls_samples(torch, lambda: mxq.mxq_fill_rows16(out),
-                                  replays=ns)
+    nxt = rotation(outs)
+    write_us = time_calls_samples(
+        torch, lambda: mxq.mxq_fill_rows16(nxt()), replays=ns)
     comb_us_graph = time_calls_samples(
-        torch, lambda: mxq.moe_combine(y, s2d, w, out=out), replays=ns)
+        torch, lambda: mxq.moe_combine(y, s2d, w, out=nxt()), replays=ns)
     # the same three with the MALL flushed before each call
     gather_cold = time_calls_cold_samples(
         torch, lambda: mxq.mxq_gather_read16(y, s2d, gather_sink), flush,
         reps=ns)
     write_cold = time_calls_cold_samples(
-        torch, lambda: mxq.mxq_fill_rows16(out), flush, reps=ns)
+        torch, lambda: mxq.mxq_fill_rows16(nxt()), flush, reps=ns)
     del flush
 
     value = B_step / (step_ms * 1e-3) / 1e9
@@ -644,8 +684,9 @@ def main():
                                              2),
                 "output_write_cold_us": round(float(np.median(write_cold)),
                                               2),
-                "note": "graph-timed medians over 100 replays of 20 calls; "
-                        "cold: MALL flushed before each call",
+                "note": "graph-timed medians over %d replays of 20 "
+                        "calls; cold: MALL flushed before each call, the "
+                        "write-back left after it charged" % ns,
             },
         },
     }
@@ -655,7 +696,7 @@ def main():
                                       H, q, B_sq, A, dev)
         srows = scatter_rows_row(torch, mxq, x, lay_out["src2dst"], R, H, q,
                                  T, K, A, dev)
-    del q, s, out
+    del q, s, out, outs
 
     if not args.no_rows:
         result["rows"] = other_rows(torch, mxq, si, dev,
@@ -1018,7 +1059,8 @@ def other_rows(torch, mxq, si, dev, cpu=True):
                        "note": "warm: the 64 MiB input stays in the 256 MB "
                                "MALL across the two passes and back-to-back "
                                "calls; cold: MALL flushed by reading 512 MB "
-                               "before each call; equal_scales: every token "
+                               "before each call, the write-back left after "
+                               "it charged; equal_scales: every token "
                                "scale 2^-3, so every row's bound is the "
                                "largest (rows holding 448 settle the max "
                                "pass at once) (warm); equal_scales_no_row_"
@@ -1128,13 +1170,15 @@ def other_rows(torch, mxq, si, dev, cpu=True):
     lay = mxq.moe_layout(idsd, 0, 128, "compact")
     yl = si.gaussian_bf16_device(505, (lay["num_rows"], 4096), dev)
     wd = torch.from_numpy(cw).to(dev)
-    ol = torch.empty((16384, 4096), dtype=torch.bfloat16, device=dev)
+    ols = [torch.empty((16384, 4096), dtype=torch.bfloat16, device=dev)
+           for _ in range(N_OUT)]
+    nxt = rotation(ols)
     byts = bytes_combine(16384, 8, 4096, 16384 * 8)
     rows["large_combine"] = {
         "workload": "T=16384, hidden 4096, 128 experts top-8, 147328-row "
                     "layout",
         **timed_row(torch, lambda: mxq.moe_combine(yl, lay["src2dst"], wd,
-                                                   out=ol),
+                                                   out=nxt()),
                     nbytes=byts, flush=flush)}
     if cpu:
         yl_h = yl.view(torch.int16).cpu().numpy().view(np.uint16)

@@ -15,14 +15,8 @@
 // kernel reads K valid rows of 2H bytes and writes one row.  Every
 // expert-output row is read exactly once, so the loads are non-temporal
 // (measured on MI355X: the prefill gather took 183 us instead of 196 us with
-// plain loads).  The output row is written with device-scope stores (SC1):
-// they pass the CU's L2 to the memory-side cache, which writes them to HBM
-// in larger runs than the writes that streaming stores interleave with the
-// gather reads.  Measured on MI355X at the prefill workload (8192 x 7168):
-// the combine 170.1 against 175.8 us with streaming stores, and the whole
-// step (layout + scatter + combine, back to back) 0.270 against 0.278 ms;
-// with the MALL flushed before each step and the write-back left after it
-// charged to the step, 0.302 against 0.307 ms.  Plain stores took 181.7 us.
+// plain loads), and the output row is written with streaming (non-temporal)
+// stores so it does not displace cached lines.
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
 
@@ -49,11 +43,6 @@ __global__ __launch_bounds__(1024) void combine_kernel(
   const int jl = min(lane, K - 1);
   const int32_t d_lane = K > 0 ? src2dst[t * K + jl] : -1;
   const int32_t w_lane = K > 0 ? __float_as_int(w[t * K + jl]) : 0;
-  // the token's output row as a bounds-checked buffer (H * 4 < 2^31,
-  // checked on the host)
-  const __amdgpu_buffer_rsrc_t orow = raw_rsrc(
-      static_cast<uint8_t*>(out) + t * ld_out * (F32_OUT ? 4 : 2),
-      (uint32_t)H * (F32_OUT ? 4 : 2));
   for (int col = threadIdx.x * 8; col < H; col += blockDim.x * 8) {
     float acc[8];
 #pragma unroll
@@ -86,17 +75,15 @@ __global__ __launch_bounds__(1024) void combine_kernel(
       }
     }
     if constexpr (F32_OUT) {
-      const uint32_t off = (uint32_t)col * 4;
-      store16_dev(orow, off,
-                  u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                        __float_as_uint(acc[2]), __float_as_uint(acc[3])});
-      store16_dev(orow, off + 16,
-                  u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
-                        __float_as_uint(acc[6]), __float_as_uint(acc[7])});
+      float* o = static_cast<float*>(out) + t * ld_out + col;
+      store16_nt(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                          __float_as_uint(acc[2]), __float_as_uint(acc[3])});
+      store16_nt(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                              __float_as_uint(acc[6]), __float_as_uint(acc[7])});
     } else {
-      store16_dev(orow, (uint32_t)col * 2,
-                  u32x4{bf16x2_rne(acc[0], acc[1]), bf16x2_rne(acc[2], acc[3]),
-                        bf16x2_rne(acc[4], acc[5]), bf16x2_rne(acc[6], acc[7])});
+      uint16_t* o = static_cast<uint16_t*>(out) + t * ld_out + col;
+      store16_nt(o, u32x4{bf16x2_rne(acc[0], acc[1]), bf16x2_rne(acc[2], acc[3]),
+                          bf16x2_rne(acc[4], acc[5]), bf16x2_rne(acc[6], acc[7])});
     }
   }
 }
@@ -124,8 +111,6 @@ extern "C" mxq_status moe_combine(const void* y_bf16, int64_t ld_y,
   const int64_t esz = out_dtype == MXQ_OUT_F32 ? 4 : 2;
   if (!aligned16(out) || (ld_out * esz) % 16 != 0)
     return MXQ_ERR_INVALID_ARGUMENT;
-  // an output row is addressed as one buffer of H * esz bytes
-  if ((int64_t)H * esz > INT32_MAX) return MXQ_ERR_UNSUPPORTED;
 
   const int threads = row_block_threads(H, 8);
   hipStream_t s = as_stream(stream);

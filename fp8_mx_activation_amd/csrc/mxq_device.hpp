@@ -42,28 +42,6 @@ __device__ __forceinline__ void store16_nt(void* p, const u32x4& v) {
   __builtin_nontemporal_store(v.w, d + 3);
 }
 
-// Raw buffer resource over `bytes` bytes at p (no stride; word 3 = 32-bit
-// data format): stores through it are bounds-checked by the hardware, an
-// offset at or past `bytes` is dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(void* p,
-                                                           uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)bytes, 0x00020000);
-}
-
-// Cache-policy operand of a buffer store: bit 4 is SC1, device scope.
-constexpr int kDeviceScope = 16;
-
-// 16-byte store at byte offset `off` of a raw buffer, device scope (SC1):
-// the data goes through the CU's L2 to the device's coherence point (the
-// memory-side cache, then HBM) instead of staying dirty in the L2 or
-// streaming past the memory-side cache.
-__device__ __forceinline__ void store16_dev(__amdgpu_buffer_rsrc_t r,
-                                            uint32_t off, const u32x4& v) {
-  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-  const u4 d = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(d, r, (int)off, 0, kDeviceScope);
-}
-
 // ---------------------------------------------------------- cross-lane max
 
 // Value held by lane (lane ^ MASK); MASK in {1, 2, 4, 8, 16}.  Masks 1 and 2
