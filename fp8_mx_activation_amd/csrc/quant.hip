@@ -50,16 +50,50 @@ enum Placement { kStrided = 0, kMfma = 1 };
 // 109.8 -> 93.1 us and 566 -> 508 MB written (tiles of 16: 105.8 -> 91.2
 // us), with the word stores below; the row-major placement keeps token
 // order (87.0 us against 92.3 us with the contiguous ranges).
+//
+// Lookahead.  Phase 1 reads with H / 16 lanes; the wavefronts after them
+// have nothing to read, so they fetch one word per 64 bytes of the row of
+// the token that block blockIdx.x + kAhead takes, if that token has a
+// destination (the same test as below).  That block runs on the same XCD
+// (kAhead is a multiple of 8) about a microsecond later and finds its row's
+// lines in flight or in L2, so reads from HBM keep more requests in flight
+// without more destination rows open for writing.  Only blocks with at
+// least kAheadMinRows rows to write look ahead: the two round trips (the
+// token's destinations, then its row) must end before the block's own
+// writes do.  The fetched words are folded into a value stored only where
+// `sink` is non-null (the launch passes null); the compiler cannot know
+// that, so the loads stay.  Measured on MI355X (graph-timed; MALL flushed
+// before each call in brackets): prefill shape 87.0-87.4 us [110.4-110.9]
+// against 87.3 us [112.0-112.7] for the same kernel without the lookahead;
+// distances 64-96 measured best (0, the block's own row, and 256 or more
+// gained less).  Its code costs short blocks a little: with 32 of 256
+// experts local (about one row per token) 23.2 against 22.2 us, still
+// below the 23.9 us of the kernel before it.  Smaller blocks (more tokens
+// in flight per CU) and one block per CU with the lookahead were measured
+// too: the first slower everywhere (121 us from HBM), the second 108 us
+// from HBM but 30.5 against 22.4 us with 32 experts local.
+constexpr int kAhead = 96;
+constexpr int kAheadMinRows = 4;
+
+template <int PLACE>
+__device__ __forceinline__ int64_t token_of_block(int64_t b, int64_t nblocks) {
+  if constexpr (PLACE == kMfma)  // nblocks is a multiple of 8
+    return (b & 7) * (nblocks >> 3) + (b >> 3);
+  return b;
+}
+
+// At most 64 VGPRs (eight waves per SIMD), so that two blocks fit on a CU
+// (one block per CU made a slice with 32 of 256 experts local 36 % slower).
 template <int G, int RULE, int PLACE>
-__global__ __launch_bounds__(1024) void scatter_quant_kernel(
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
+void scatter_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, int32_t H, int64_t T,
     const int32_t* __restrict__ src2dst, int32_t K, uint8_t* __restrict__ q,
     int64_t ld_q, uint8_t* __restrict__ s, int64_t s_rs, int64_t s_c4,
-    int64_t num_rows) {
+    int64_t num_rows, uint32_t* __restrict__ sink) {
   extern __shared__ __align__(16) uint8_t row[];  // [H] fp8, then [H/G] scales
-  int64_t t = blockIdx.x;
-  if constexpr (PLACE == kMfma) {  // gridDim.x is a multiple of 8
-    t = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int64_t t = token_of_block<PLACE>(blockIdx.x, gridDim.x);
+  if constexpr (PLACE == kMfma) {
     if (t >= T) return;
   }
   // lane j of every wavefront loads destination j (K <= 64) in one vector
@@ -68,7 +102,26 @@ __global__ __launch_bounds__(1024) void scatter_quant_kernel(
   const int lane = threadIdx.x & 63;
   const int32_t d_lane = src2dst[t * K + min(lane, K - 1)];
   const bool valid = lane < K && d_lane >= 0 && (int64_t)d_lane < num_rows;
-  if (__ballot(valid) == 0) return;  // the same in every wavefront
+  const uint64_t has = __ballot(valid);
+  if (has == 0) return;  // the same in every wavefront
+  // lookahead by the wavefronts with no channels in phase 1, in blocks
+  // with enough rows to write that it ends before they do
+  const int p0 = ((H / 16 + 63) / 64) * 64;
+  uint32_t pf = 0;
+  if ((int)threadIdx.x >= p0 && __popcll(has) >= kAheadMinRows &&
+      (int64_t)blockIdx.x + kAhead < (int64_t)gridDim.x) {
+    const int64_t t2 =
+        token_of_block<PLACE>((int64_t)blockIdx.x + kAhead, gridDim.x);
+    if (t2 < T) {
+      const int32_t d2 = src2dst[t2 * K + min(lane, K - 1)];
+      if (__ballot(lane < K && d2 >= 0 && (int64_t)d2 < num_rows) != 0) {
+        const int64_t off = (int64_t)(threadIdx.x - p0) * 64;
+        if (off + 4 <= (int64_t)H * 2)
+          pf = *reinterpret_cast<const uint32_t*>(
+              reinterpret_cast<const uint8_t*>(x + t2 * ld_x) + off);
+      }
+    }
+  }
   const uint16_t* xr = x + t * ld_x;
   const bool lead = (threadIdx.x & (G / 16 - 1)) == 0;
   for (int col = threadIdx.x * 16; col < H; col += blockDim.x * 16) {
@@ -112,10 +165,14 @@ __global__ __launch_bounds__(1024) void scatter_quant_kernel(
         }
       }
     } else {
+      // not unrolled: unrolled, its 64-bit addresses pushed the kernel past
+      // 64 VGPRs
+#pragma unroll 1
       for (int g = lane; g < ng; g += 64)
         s[scale_addr(d, g, s_rs, s_c4)] = row[H + g];
     }
   }
+  if (sink != nullptr) sink[threadIdx.x] = pf;
 }
 
 // Send-side quant for more than 64 segments.  Segment g owns blocks
@@ -265,10 +322,10 @@ void launch_scatter(int rule, unsigned T, int threads, size_t lds,
   const unsigned grid = PLACE == kMfma ? (T + 7) / 8 * 8 : T;
   if (rule == MXQ_RULE_OCP_FLOOR)
     scatter_quant_kernel<G, kOcpFloor, PLACE><<<grid, threads, lds, s>>>(
-        x, ld_x, H, T, src2dst, K, q, ld_q, sc, rs, c4, num_rows);
+        x, ld_x, H, T, src2dst, K, q, ld_q, sc, rs, c4, num_rows, nullptr);
   else
     scatter_quant_kernel<G, kNoClip, PLACE><<<grid, threads, lds, s>>>(
-        x, ld_x, H, T, src2dst, K, q, ld_q, sc, rs, c4, num_rows);
+        x, ld_x, H, T, src2dst, K, q, ld_q, sc, rs, c4, num_rows, nullptr);
 }
 
 // Launch of the send-side quant: up to 64 segments the unit kernel with a

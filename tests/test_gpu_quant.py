@@ -78,6 +78,23 @@ def test_ragged_widths(ora, G, H):
     scatter_both(ora, x, ids, 9, "compact", G, block_e=16)
 
 
+@pytest.mark.parametrize("H,G,pad", [(7168, 128, (0, 0, 0)),
+                                     (12288, 32, (8, 16, 3)),
+                                     (16384 + 128, 128, (0, 0, 0)),
+                                     (640, 32, (24, 0, 1))])
+def test_lookahead_mixed_destinations(ora, H, G, pad):
+    """More tokens than the scatter's lookahead distance (96 blocks), zero
+    to eight local destinations per token (16 of 32 experts local, so some
+    blocks look ahead and some do not), and widths whose idle wavefronts
+    cover the whole next row (7168, 640), part of it (12288) or none
+    (16512).  The lookahead only loads, so every byte still matches."""
+    rng = np.random.default_rng(H + G)
+    T = 300
+    x = si.gaussian_bf16(rng, (T, H))
+    ids = si.uniform_topk(rng, T, 32, 8)
+    scatter_both(ora, x, ids, 16, "compact", G, ld_pad=pad, block_e=16)
+
+
 def test_padded_strides(ora):
     rng = np.random.default_rng(5)
     x = si.gaussian_bf16(rng, (70, 640))
