@@ -176,6 +176,8 @@ SAMPLES = 100  # set from --samples in main()
 
 # output buffers a combine timing rotates over (see the step's setup)
 N_OUT = 4
+# token-row copies of the step with its rows read from HBM
+N_X = 3
 
 
 def rotation(bufs):
@@ -454,6 +456,28 @@ def main():
     if status != 0:
         raise RuntimeError("a library call in the event-free pass failed")
 
+    # the same steps with the token rows rotating over N_X copies (351 MB,
+    # more than the MALL), so that every step's scatter reads its rows from
+    # HBM: wall clock, no events, no flushes -- the steady state when the
+    # activations handed over are no longer cached
+    xs = [x] + [x.clone() for _ in range(N_X - 1)]
+    sq_argv = [(xx.data_ptr(),) + sq_args[1:] for xx in xs]
+    for i in range(2 * N_X * N_OUT):
+        status |= L.moe_layout(*lay_args)
+        status |= L.moe_scatter_quant(*sq_argv[i % N_X])
+        status |= L.moe_combine(*cb_argv[i % N_OUT])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        status |= L.moe_layout(*lay_args)
+        status |= L.moe_scatter_quant(*sq_argv[i % N_X])
+        status |= L.moe_combine(*cb_argv[i % N_OUT])
+    torch.cuda.synchronize()
+    hbm_rows_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    if status != 0:
+        raise RuntimeError("a library call in the rotating-rows pass failed")
+    del xs, sq_argv
+
     # per-kernel pass: the same steps with events around each kernel, at
     # least 100 of them whatever --steps is, for the spread of each kernel
     n_k = max(args.steps, args.samples)
@@ -602,6 +626,17 @@ def main():
         "moe_combine_us_in_timed_region": round(
             1e3 * float(np.mean(cb_ms)), 2),
         "ms_per_step_without_events": round(noev_step_ms, 4),
+        "step_token_rows_from_hbm": {
+            "note": "the same steps by wall clock, without events, with the "
+                    "token rows rotating over %d copies (more than the 256 "
+                    "MB MALL) so that every scatter reads them from HBM" %
+                    N_X,
+            "ms_per_step": round(hbm_rows_step_ms, 4),
+            "gbs": round(B_step / (hbm_rows_step_ms * 1e-3) / 1e9, 2),
+            "pct_of_peak": round(
+                100 * B_step / (hbm_rows_step_ms * 1e-3) / 1e9 /
+                PEAK_HBM_GBS, 2),
+        },
         "scatter_quant_plus_combine": {
             "bytes": B_sq + B_cb,
             "us": round(float(np.median(sq_us) + np.median(kcb_us)), 2),
@@ -668,6 +703,15 @@ def main():
                     float(np.percentile(frac_cold, 10)), 4),
                 "frac_mall_flushed_p90": round(
                     float(np.percentile(frac_cold, 90)), 4),
+            },
+            # the best copy kernel of this run (16-byte vectors,
+            # non-temporal loads and stores, 1 GiB read + 1 GiB written):
+            # the rate the box sustains on a 1:1 read/write mix
+            "same_run_copy_bound": {
+                "copy16_gbs": copy16["nontemporal_loads_and_stores"],
+                "combine_gbs": round(cb_gbs, 2),
+                "combine_over_copy": round(
+                    cb_gbs / copy16["nontemporal_loads_and_stores"], 4),
             },
             # the combine beside its own two halves measured in this run
             "combine_same_run_halves": {
