@@ -52,27 +52,34 @@ enum Placement { kStrided = 0, kMfma = 1 };
 // order (87.0 us against 92.3 us with the contiguous ranges).
 //
 // Lookahead.  Phase 1 reads with H / 16 lanes; the wavefronts after them
-// have nothing to read, so they fetch one word per 64 bytes of the row of
-// the token that block blockIdx.x + kAhead takes, if that token has a
-// destination (the same test as below).  That block runs on the same XCD
-// (kAhead is a multiple of 8) about a microsecond later and finds its row's
-// lines in flight or in L2, so reads from HBM keep more requests in flight
-// without more destination rows open for writing.  Only blocks with at
-// least kAheadMinRows rows to write look ahead: the two round trips (the
+// have nothing to read, so they fetch one word per 128 bytes (one L2 line)
+// of the rows of the tokens that blocks blockIdx.x + kAhead and
+// blockIdx.x + 2 * kAhead take, if those tokens have a destination (the
+// same test as below): two wavefronts per row at H = 7168, 4 of the 9 idle
+// ones.  Those blocks run on the same XCD (kAhead is a multiple of 8) one
+// and two microseconds later and find their rows' lines in flight or in
+// L2, so reads from HBM keep more requests in flight without more
+// destination rows open for writing.  Only blocks with at least
+// kAheadMinRows rows to write look ahead: the two round trips (the
 // token's destinations, then its row) must end before the block's own
 // writes do.  The fetched words are folded into a value stored only where
 // `sink` is non-null (the launch passes null); the compiler cannot know
 // that, so the loads stay.  Measured on MI355X (graph-timed; MALL flushed
-// before each call in brackets): prefill shape 87.0-87.4 us [110.4-110.9]
-// against 87.3 us [112.0-112.7] for the same kernel without the lookahead;
-// distances 64-96 measured best (0, the block's own row, and 256 or more
-// gained less).  Its code costs short blocks a little: with 32 of 256
-// experts local (about one row per token) 23.2 against 22.2 us, still
-// below the 23.9 us of the kernel before it.  Smaller blocks (more tokens
-// in flight per CU) and one block per CU with the lookahead were measured
-// too: the first slower everywhere (121 us from HBM), the second 108 us
-// from HBM but 30.5 against 22.4 us with 32 experts local.
+// before each call, write-back charged, in brackets), prefill shape:
+// 87.3-87.4 us [108.4-109.8] against 87.6 us [110.4-111.7] with one row
+// ahead at one word per 64 bytes and 87.3 us [112.0-112.7] without
+// lookahead.  Four rows ahead measured 107.5-108.2 us from HBM but cost a
+// slice with 128 of 256 experts local 2 us (67.1 against 65.0 us); one row
+// at distance 64 or 128, or two at 64/128 or 128/256, gained less.  With 32
+// of 256 experts local (about one row per token) the kernel takes 23.0 us
+// against 22.2 us without any lookahead code and 23.9 us for the kernel
+// before it.  Smaller blocks (more tokens in flight per CU) and one block
+// per CU were measured too: the first slower everywhere (121 us from HBM),
+// the second 108 us from HBM with one row ahead but 30.5 against 22.4 us
+// with 32 experts local.
 constexpr int kAhead = 96;
+constexpr int kAheadRows = 2;
+constexpr int kAheadStride = 128;
 constexpr int kAheadMinRows = 4;
 
 template <int PLACE>
@@ -104,21 +111,26 @@ void scatter_quant_kernel(
   const bool valid = lane < K && d_lane >= 0 && (int64_t)d_lane < num_rows;
   const uint64_t has = __ballot(valid);
   if (has == 0) return;  // the same in every wavefront
-  // lookahead by the wavefronts with no channels in phase 1, in blocks
-  // with enough rows to write that it ends before they do
+  // lookahead by the wavefronts with no channels in phase 1: wpr of them
+  // per row ahead, kAheadRows rows
   const int p0 = ((H / 16 + 63) / 64) * 64;
   uint32_t pf = 0;
-  if ((int)threadIdx.x >= p0 && __popcll(has) >= kAheadMinRows &&
-      (int64_t)blockIdx.x + kAhead < (int64_t)gridDim.x) {
-    const int64_t t2 =
-        token_of_block<PLACE>((int64_t)blockIdx.x + kAhead, gridDim.x);
-    if (t2 < T) {
-      const int32_t d2 = src2dst[t2 * K + min(lane, K - 1)];
-      if (__ballot(lane < K && d2 >= 0 && (int64_t)d2 < num_rows) != 0) {
-        const int64_t off = (int64_t)(threadIdx.x - p0) * 64;
-        if (off + 4 <= (int64_t)H * 2)
-          pf = *reinterpret_cast<const uint32_t*>(
-              reinterpret_cast<const uint8_t*>(x + t2 * ld_x) + off);
+  if ((int)threadIdx.x >= p0 && __popcll(has) >= kAheadMinRows) {
+    const int wi = ((int)threadIdx.x - p0) >> 6;
+    const int wpr = (H * 2 / kAheadStride + 63) / 64;
+    const int which = wpr > 0 ? wi / wpr : kAheadRows;
+    const int64_t b2 = (int64_t)blockIdx.x + (int64_t)kAhead * (which + 1);
+    if (which < kAheadRows && b2 < (int64_t)gridDim.x) {
+      const int64_t t2 = token_of_block<PLACE>(b2, gridDim.x);
+      if (t2 < T) {
+        const int32_t d2 = src2dst[t2 * K + min(lane, K - 1)];
+        if (__ballot(lane < K && d2 >= 0 && (int64_t)d2 < num_rows) != 0) {
+          const int64_t off =
+              (int64_t)((wi - which * wpr) * 64 + lane) * kAheadStride;
+          if (off + 4 <= (int64_t)H * 2)
+            pf = *reinterpret_cast<const uint32_t*>(
+                reinterpret_cast<const uint8_t*>(x + t2 * ld_x) + off);
+        }
       }
     }
   }
