@@ -226,8 +226,8 @@ __global__ __launch_bounds__(1024) void live_rows_kernel(
   }
 }
 
-// Send-side quant for up to 64 segments, with a grid of about one block
-// per CU that does not grow with the padded buffer.  Lane g of every
+// Send-side quant for up to 64 segments, with a grid of 4096 wavefronts
+// that does not grow with the padded buffer.  Lane g of every
 // wavefront holds segment g's live count (clipped to [0, rps]) and their
 // inclusive prefix, so live row i (in segment order) lies in segment
 // g = #{segments whose prefix <= i}, one ballot.  Work comes in units of
@@ -238,12 +238,18 @@ __global__ __launch_bounds__(1024) void live_rows_kernel(
 // group 32, graph-timed): 112 live rows 2.9 us (3.7 us with a block per
 // padded row group), all rows live 97.6 us (102.1 us); two or four units
 // per wavefront and round were slower with many rows live (103.3 and
-// 108.0 us).  The launch alone costs about 2.1 us per call here (an empty
-// kernel measured the same), which is what an all-empty batch costs.
+// 108.0 us).  The 4096 wavefronts come in blocks of two: 14 x 8 live rows
+// 2.65 us, empty 2.16 us, all live 97.0 us, against 2.81 / 2.14 / 97.0 us
+// in blocks of 16 (256 x 1024), 2.75 / 2.06 / 96.1 us in blocks of 4 and
+// 2.81 / 2.55 / 97.8 us in blocks of one; with half as many wavefronts all
+// live took 100-104 us.  The launch alone costs about 2.1 us per call
+// here (an empty kernel measured the same), which is what an all-empty
+// batch costs.
 constexpr int kLiveChunk = 1024;  // channels of one unit (64 lanes x 16)
+constexpr int kLiveThreads = 128;
 
 template <int G, int RULE, int PLACE>
-__global__ __launch_bounds__(1024) void live_units_kernel(
+__global__ __launch_bounds__(kLiveThreads) void live_units_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, int64_t rps, int32_t nseg,
     const int32_t* __restrict__ live, int32_t H, int32_t upr,
     uint8_t* __restrict__ q, int64_t ld_q, uint8_t* __restrict__ s,
@@ -341,10 +347,10 @@ void launch_scatter(int rule, unsigned T, int threads, size_t lds,
 }
 
 // Launch of the send-side quant: up to 64 segments the unit kernel with a
-// grid of at most kLiveBlocks blocks of 1024 threads, fewer when the padded
-// buffer holds fewer units; above 64 segments the row kernel with about
-// 1024 blocks over the segments.
-constexpr int kLiveBlocks = 256;
+// grid of at most kLiveBlocks blocks of kLiveThreads threads, fewer when
+// the padded buffer holds fewer units; above 64 segments the row kernel
+// with about 1024 blocks over the segments.
+constexpr int kLiveBlocks = 2048;
 constexpr int kLiveUnitSegments = 64;
 
 template <int G, int RULE, int PLACE>
@@ -355,9 +361,10 @@ void launch_live_rule(hipStream_t s, const uint16_t* x, int64_t ld_x,
   if (nseg <= kLiveUnitSegments) {
     const int32_t upr = (int32_t)ceil_div(H, kLiveChunk);
     const int64_t max_units = (int64_t)nseg * rps * upr;
-    int64_t blocks = ceil_div(max_units, 16);
+    int64_t blocks = ceil_div(max_units, kLiveThreads / 64);
     if (blocks > kLiveBlocks) blocks = kLiveBlocks;
-    live_units_kernel<G, RULE, PLACE><<<(unsigned)blocks, 1024, 0, s>>>(
+    live_units_kernel<G, RULE, PLACE><<<(unsigned)blocks, kLiveThreads, 0,
+                                        s>>>(
         x, ld_x, rps, nseg, live, H, upr, q, ld_q, sc, rs, c4);
     return;
   }
