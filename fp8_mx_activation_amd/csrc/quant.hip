@@ -53,34 +53,40 @@ enum Placement { kStrided = 0, kMfma = 1 };
 //
 // Lookahead.  Phase 1 reads with H / 16 lanes; the wavefronts after them
 // have nothing to read, so they fetch one word per 128 bytes (one L2 line)
-// of the rows of the tokens that blocks blockIdx.x + kAhead and
-// blockIdx.x + 2 * kAhead take, if those tokens have a destination (the
-// same test as below): two wavefronts per row at H = 7168, 4 of the 9 idle
-// ones.  Those blocks run on the same XCD (kAhead is a multiple of 8) one
-// and two microseconds later and find their rows' lines in flight or in
-// L2, so reads from HBM keep more requests in flight without more
-// destination rows open for writing.  Only blocks with at least
-// kAheadMinRows rows to write look ahead: the two round trips (the
-// token's destinations, then its row) must end before the block's own
-// writes do.  The fetched words are folded into a value stored only where
-// `sink` is non-null (the launch passes null); the compiler cannot know
-// that, so the loads stay.  Measured on MI355X (graph-timed; MALL flushed
-// before each call, write-back charged, in brackets), prefill shape:
-// 87.3-87.4 us [108.4-109.8] against 87.6 us [110.4-111.7] with one row
-// ahead at one word per 64 bytes and 87.3 us [112.0-112.7] without
-// lookahead.  Four rows ahead measured 107.5-108.2 us from HBM but cost a
-// slice with 128 of 256 experts local 2 us (67.1 against 65.0 us); one row
-// at distance 64 or 128, or two at 64/128 or 128/256, gained less.  With 32
-// of 256 experts local (about one row per token) the kernel takes 23.0 us
-// against 22.2 us without any lookahead code and 23.9 us for the kernel
-// before it.  Smaller blocks (more tokens in flight per CU) and one block
-// per CU were measured too: the first slower everywhere (121 us from HBM),
-// the second 108 us from HBM with one row ahead but 30.5 against 22.4 us
-// with 32 experts local.
+// of the rows of the tokens that blocks blockIdx.x + kAhead,
+// blockIdx.x + 2 * kAhead, ... take, if those tokens have a destination
+// (the same test as below): two wavefronts per row at H = 7168.  Those
+// blocks run on the same XCD (kAhead is a multiple of 8) one, two, ...
+// microseconds later and find their rows' lines in flight or in L2, so
+// reads from HBM keep more requests in flight without more destination
+// rows open for writing.  The depth follows the rows the block writes,
+// which set how long it stays resident: none below kAheadMinRows (the two
+// round trips, the token's destinations and then its row, must end before
+// the block's own writes do), two rows ahead from kAheadMinRows, four from
+// kAheadDeepRows.  The fetched words are folded into a value stored only
+// where `sink` is non-null (the launch passes null); the compiler cannot
+// know that, so the loads stay.  Measured on MI355X (graph-timed; MALL
+// flushed before each call, write-back charged, in brackets), prefill
+// shape (eight rows per token): 86.6-86.7 us [107.0-107.9] against 87.1 us
+// [108.7-109.1] with two rows ahead for every block of four or more rows,
+// 87.6 us [110.4-111.7] with one row ahead at one word per 64 bytes and
+// 87.3 us [112.0-112.7] without lookahead.  Four rows ahead from six rows
+// gained 0.5 us more there but cost a slice with 192 of 256 experts local
+// (six rows per token on average) 2 us from HBM; from seven rows that
+// slice takes 91.6-92.0 against 90.7-91.1 us with two rows ahead.  Four
+// rows ahead from four rows cost a slice with 128 local 2 us (67.1 against
+// 65.0 us).  With 32 of 256 experts local (about one row per token) the
+// kernel takes 23.0-23.1 us against 22.2 us without any lookahead code and
+// 23.9 us for the kernel before it.  Smaller blocks (more tokens in flight
+// per CU) and one block per CU were measured too: the first slower
+// everywhere (121 us from HBM), the second 108 us from HBM with one row
+// ahead but 30.5 against 22.4 us with 32 experts local.
 constexpr int kAhead = 96;
 constexpr int kAheadRows = 2;
+constexpr int kAheadRowsDeep = 4;
 constexpr int kAheadStride = 128;
 constexpr int kAheadMinRows = 4;
+constexpr int kAheadDeepRows = 7;
 
 template <int PLACE>
 __device__ __forceinline__ int64_t token_of_block(int64_t b, int64_t nblocks) {
@@ -112,15 +118,18 @@ void scatter_quant_kernel(
   const uint64_t has = __ballot(valid);
   if (has == 0) return;  // the same in every wavefront
   // lookahead by the wavefronts with no channels in phase 1: wpr of them
-  // per row ahead, kAheadRows rows
+  // per row ahead, two or four rows
   const int p0 = ((H / 16 + 63) / 64) * 64;
   uint32_t pf = 0;
-  if ((int)threadIdx.x >= p0 && __popcll(has) >= kAheadMinRows) {
+  const int nrows = __popcll(has);
+  if ((int)threadIdx.x >= p0 && nrows >= kAheadMinRows) {
     const int wi = ((int)threadIdx.x - p0) >> 6;
     const int wpr = (H * 2 / kAheadStride + 63) / 64;
-    const int which = wpr > 0 ? wi / wpr : kAheadRows;
+    const int rows_ahead = nrows >= kAheadDeepRows ? kAheadRowsDeep
+                                                   : kAheadRows;
+    const int which = wpr > 0 ? wi / wpr : rows_ahead;
     const int64_t b2 = (int64_t)blockIdx.x + (int64_t)kAhead * (which + 1);
-    if (which < kAheadRows && b2 < (int64_t)gridDim.x) {
+    if (which < rows_ahead && b2 < (int64_t)gridDim.x) {
       const int64_t t2 = token_of_block<PLACE>(b2, gridDim.x);
       if (t2 < T) {
         const int32_t d2 = src2dst[t2 * K + min(lane, K - 1)];
