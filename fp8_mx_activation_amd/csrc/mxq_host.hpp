@@ -74,6 +74,19 @@ inline LayoutGeom layout_geom(int64_t A) {
 // wavefront); above it the histogram + slots pair over chunks is faster.
 constexpr int64_t kSingleMax = 4096;
 
+// Within kSingleMax, up to this many tokens the layout takes one block per
+// token instead (each block counts the whole routing and places its own
+// assignments): up to 2048 tokens with blocks of 256 threads (at most 256
+// local experts), up to 1024 with blocks of 1024 (more experts, which the
+// region scan spreads one per thread).
+constexpr int64_t kTokenMaxTokens = 2048;
+constexpr int64_t kTokenMaxTokensWide = 1024;
+
+inline bool layout_per_token(int64_t A, int64_t T, int32_t E) {
+  return A > 0 && A <= kSingleMax &&
+         T <= (E <= 256 ? kTokenMaxTokens : kTokenMaxTokensWide);
+}
+
 // Above kSingleMax and up to these sizes the slot kernel still runs alone:
 // each of its blocks counts the whole routing into LDS itself (its 16
 // wavefronts keep private counts), so the histogram launch and its per-chunk

@@ -130,6 +130,26 @@ def test_single_launch_boundary(ora, T, K, E):
     got, ref = run_both(ora, ids, 0, E, "masked", cap=max(1, T * K // E // 2))
 
 
+@pytest.mark.parametrize("T,K,E", [(2048, 2, 256), (2049, 1, 256),
+                                   (1024, 4, 300), (1025, 3, 300),
+                                   (1, 64, 1024), (1, 1, 1), (7, 64, 64)])
+def test_per_token_boundary(ora, T, K, E):
+    """Around the switch from one block per token (up to 2048 tokens with at
+    most 256 experts, up to 1024 with more) to one block ranking the whole
+    routing, at most 4096 assignments: 2048 x 2 and 1024 x 4 over 300
+    experts take a block per token, 2049 x 1 and 1025 x 3 over 300 the
+    single ranking block; one token with 64 assignments; duplicates of an
+    expert inside one token (7 x 64 over 64 experts)."""
+    rng = np.random.default_rng(T * 131 + K * 7 + E)
+    ids = si.zipf_topk(rng, T, E, K) if E >= 2 * K else si.uniform_topk(
+        rng, T, E, K)
+    if T == 7:
+        ids[:, 1::2] = ids[:, 0:1]  # the same expert in half of a token
+    run_both(ora, ids, 0, E, "compact")
+    run_both(ora, ids, 0, E, "compact", block_e=1)
+    run_both(ora, ids, 0, E, "masked", cap=max(1, T * K // E // 2))
+
+
 @pytest.mark.parametrize("T,K,E", [(4097, 1, 256), (4097, 1, 257),
                                    (2048, 8, 256), (2049, 8, 256),
                                    (2048, 8, 128), (1024, 8, 32),
