@@ -71,6 +71,20 @@ def test_scatter_mfma_placement(ora, tm, rule, G, H):
 
 
 @pytest.mark.parametrize("tm", [32, 16])
+def test_mfma_placement_lookahead(ora, tm):
+    """More tokens than the scatter's lookahead distance with the MFMA
+    placement's token order (each XCD takes a contiguous range; 300 tokens
+    make a grid of 304 blocks, so the last range is short), and zero to
+    eight local destinations per token (16 of 32 experts local)."""
+    rng = np.random.default_rng(303 + tm)
+    T, H, G = 300, 2048, 128
+    x = clip_band_bf16(rng, T, H, G)
+    ids = si.uniform_topk(rng, T, 32, 8)
+    lay = ora.moe_layout(ids, 0, 16, "compact", block_e=32)
+    run_scatter(ora, x, lay["src2dst"], lay["num_rows"], G, "no_clip", tm)
+
+
+@pytest.mark.parametrize("tm", [32, 16])
 def test_prefill_mfma_placement(ora, tm):
     """The full prefill workload (8192 x 7168, 65536 assignments into 98048
     rows, UE8M0 group 128)."""
