@@ -63,7 +63,7 @@ def test_tiny_compact(ora):
 
 def test_largest_routing_compact_and_masked(ora):
     """4096 assignments (512 tokens of top-8 over 256 experts), the most
-    the fused launch takes; several 1024-id rounds per block."""
+    the fused launch takes; each thread loads several of the ids."""
     rng = np.random.default_rng(31)
     T, K, H = 512, 8, 1024
     x = si.gaussian_bf16(rng, (T, H))
@@ -88,7 +88,7 @@ def test_overflow_duplicates_and_k1(ora):
 
 def test_many_experts_wide_rows_and_extra_rows(ora):
     """1024 local experts (LDS tables at their largest) with and without
-    m_indices and with a num_rows above the bound; hidden 32768 (two row
+    m_indices and with a num_rows above the bound; hidden 32768 (four row
     chunks per lane) over 16 experts."""
     rng = np.random.default_rng(33)
     T, K = 64, 8
@@ -101,6 +101,19 @@ def test_many_experts_wide_rows_and_extra_rows(ora):
     ids16 = si.uniform_topk(rng, T, 16, K)
     xw = si.gaussian_bf16(rng, (T, 32768))
     fused_case(ora, xw, ids16, 0, 16, "compact", 128)
+
+
+def test_block_size_boundary(ora):
+    """512 local experts (the last count a 512-thread block scans) and 513
+    (the first on 1024 threads), with rows wider than one pass of either
+    block, and local ids spread over the whole window."""
+    rng = np.random.default_rng(34)
+    T, K, H = 40, 8, 17408
+    x = si.gaussian_bf16(rng, (T, H))
+    ids = si.uniform_topk(rng, T, 1024, K)
+    for E in (512, 513):
+        fused_case(ora, x, ids, 0, E, "compact", 128)
+        fused_case(ora, x, ids, 511, E, "masked", 32, cap=2)
 
 
 def test_same_as_two_calls_and_limits():
