@@ -56,6 +56,34 @@ def test_shapes(ora, rb, cols, dt, in_cm, out_cm):
     run(ora, x, lay["src2dst"], lay["num_rows"], sc, in_cm, out_cm)
 
 
+@pytest.mark.parametrize("rb,cols,dt,in_cm,out_cm", [
+    (49168, 130, np.uint8, False, False), (65584, 70, np.float32, True, True)])
+def test_rows_over_one_chunk_and_many_scale_entries(ora, rb, cols, dt, in_cm,
+                                                    out_cm):
+    """Rows that pass through LDS in two and three chunks (32 KB, then a
+    ragged tail), and more than 64 scale entries per row (entries past the
+    first 64 are fetched by the writing wavefront)."""
+    rng = np.random.default_rng(rb)
+    T, K, E = 40, 6, 20
+    ids = si.uniform_topk(rng, T, 24, K)
+    lay = ora.moe_layout(ids, 0, E, "compact", block_e=1)
+    x = si.random_e4m3_bytes(rng, (T, rb))
+    sc = rng.integers(1, 250, (T, cols)).astype(dt)
+    run(ora, x, lay["src2dst"], lay["num_rows"], sc, in_cm, out_cm)
+
+
+def test_more_destinations_than_wavefronts(ora):
+    """Top-20 routing: a token's destinations outnumber the block's eight
+    wavefronts, so wavefronts write several rows each."""
+    rng = np.random.default_rng(35)
+    T, K, E = 50, 20, 30
+    ids = si.uniform_topk(rng, T, 32, K)
+    lay = ora.moe_layout(ids, 0, E, "compact", block_e=16)
+    x = si.random_e4m3_bytes(rng, (T, 1024))
+    sc = rng.integers(1, 250, (T, 8)).astype(np.uint8)
+    run(ora, x, lay["src2dst"], lay["num_rows"], sc)
+
+
 def test_prefill_quantized_rows_equal_fused_scatter(ora):
     """The full prefill workload: quantizing every token row (the sender's
     job) and scattering the fp8 rows and scale bytes gives exactly what the
