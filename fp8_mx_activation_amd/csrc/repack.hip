@@ -473,9 +473,9 @@ __global__ __launch_bounds__(kRowsThreads) void scatter_rows_kernel(
   const int32_t d_lane = src2dst[t * K + min(lane, K - 1)];
   const bool valid = lane < K && d_lane >= 0 && (int64_t)d_lane < num_rows;
   if (__ballot(valid) == 0) return;  // the same in every wavefront
-  const uint8_t* xsr = xs + t * xs_rs;
+  const uint8_t* xsr = xs != nullptr ? xs + t * xs_rs : nullptr;
   const uint32_t s_own =
-      (xs != nullptr && lane < s_cols)
+      (xsr != nullptr && lane < s_cols)
           ? load_entry(xsr + (int64_t)lane * xs_cs, s_elem)
           : 0;
   const uint8_t* src = x + t * ld_x;
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kRowsThreads) void scatter_rows_kernel(
     }
     __syncthreads();
   }
-  if (xs == nullptr) return;
+  if (xsr == nullptr) return;
   for (int j = wave; j < K; j += kRowsThreads / 64) {
     const int64_t d = __builtin_amdgcn_readlane(d_lane, j);
     if (d < 0 || d >= num_rows) continue;
