@@ -9,12 +9,14 @@
 // rounded to bf16 (nearest even) or stored as fp32.
 //
 // One block per token and slice of channels; a lane owns 8 consecutive
-// channels.  A slice is the whole row when there are at least 256 tokens;
-// with fewer tokens than CUs each token's row is dealt to blocks of 1024
-// channels (128 threads), so that more CUs issue its loads (measured on
-// MI355X, hidden 7168, top-8: T = 128 3.25 against 3.52 us, T = 32 2.8
-// against 3.2 us; at T = 512 slices of 1024, 1792 or 3584 channels gained
-// nothing, and at T = 2048 they lost up to 7 %).  The token's
+// channels.  A slice is the whole row above 192 tokens; with at most 192
+// tokens (fewer than the 256 CUs) each token's row is dealt to blocks of
+// 1024 channels (128 threads), so that more CUs issue its loads.  Measured
+// on MI355X, hidden 7168, top-8, A/B in one process: all 256 experts local
+// T = 16 3.1 against 3.9 us, T = 128 3.6 against 4.2-4.4 us, T = 192 4.5
+// against 4.7 us, T = 255 6.0 against 5.5 us (so not there); the decode
+// slab (T = 128, 32 of 256 local) 3.2 against 3.5 us; T = 8192 178.6 us
+// either way.  The token's
 // indices and weights arrive in one vector load each (lane j holds entry j),
 // and the K rows are then loaded as independent 16-byte vectors before any
 // arithmetic, so each lane has up to eight loads in flight.  Per token the
@@ -98,9 +100,9 @@ __global__ __launch_bounds__(1024) void combine_kernel(
   }
 }
 
-// Below this many tokens a row is split into slices of kCombineSlice
+// Up to this many tokens a row is split into slices of kCombineSlice
 // channels, one block each.
-constexpr int64_t kCombineSliceTokens = 256;
+constexpr int64_t kCombineSliceMaxTokens = 192;
 constexpr int32_t kCombineSlice = 1024;
 
 }  // namespace
@@ -127,7 +129,7 @@ extern "C" mxq_status moe_combine(const void* y_bf16, int64_t ld_y,
   if (!aligned16(out) || (ld_out * esz) % 16 != 0)
     return MXQ_ERR_INVALID_ARGUMENT;
 
-  const int32_t slice = T < kCombineSliceTokens && H > kCombineSlice
+  const int32_t slice = T <= kCombineSliceMaxTokens && H > kCombineSlice
                             ? kCombineSlice
                             : H;
   const dim3 grid((unsigned)T, (unsigned)ceil_div(H, slice));

@@ -266,3 +266,22 @@ def test_no_local_assignment_gives_zero(ora):
     w = np.ones((10, 4), np.float32)
     out = combine_both(ora, bf16_to_dev(y), s2d, w, y_host=y)
     assert (bf16_to_host(out) == 0).all()
+
+
+@pytest.mark.parametrize("T,H", [(1, 1032), (192, 1032), (193, 1032),
+                                 (192, 7168), (193, 7168), (5, 1024)])
+def test_row_slices_and_their_boundary(ora, T, H):
+    """Up to 192 tokens a row is combined in slices of 1024 channels, one
+    block each (H = 1032: a last slice of 8 channels; H = 1024: one slice);
+    from 193 tokens one block takes the whole row.  Both out dtypes, every
+    token compared, out-of-range entries skipped."""
+    rng = np.random.default_rng(T * 7 + H)
+    K = 8
+    ids = si.uniform_topk(rng, T, 64, K)
+    ref, y = layout_and_outputs(ora, ids, 48, "compact", H, T + H)
+    s2d = ref["src2dst"].copy()
+    s2d[::7, 2] = ref["num_rows"] + 3
+    w = si.softmax_weights(rng, T, K)
+    yd = bf16_to_dev(y)
+    combine_both(ora, yd, s2d, w, y_host=y)
+    combine_both(ora, yd, s2d, w, out_dtype=torch.float32, y_host=y)
