@@ -41,7 +41,16 @@ __device__ __forceinline__ int64_t psum_count(const int32_t* psum, int e,
   return c > 0 ? c : 0;
 }
 
-__global__ __launch_bounds__(1024) void m_indices_from_psum_kernel(
+// One row per thread and pass: each row's expert is a binary search over the
+// starts in LDS, a chain of dependent LDS reads, so rows are spread over as
+// many threads as possible (at most kPsumBlocks blocks of kPsumThreads).
+// Measured on MI355X: 3968 rows over 32 experts 2.6 us, 80000 rows over 256
+// experts 3.0 us, against 3.9 and 5.0 us with 1024-thread blocks of four
+// rows per thread.
+constexpr int kPsumThreads = 256;
+constexpr int64_t kPsumBlocks = 1024;
+
+__global__ __launch_bounds__(kPsumThreads) void m_indices_from_psum_kernel(
     const int32_t* __restrict__ psum, int32_t E, int32_t align,
     int64_t num_rows, int32_t* __restrict__ m_indices) {
   extern __shared__ int64_t rng[];  // [E] starts, [E] ends
@@ -556,9 +565,9 @@ extern "C" mxq_status moe_m_indices_from_psum(const int32_t* psum, int32_t E,
     return MXQ_ERR_INVALID_ARGUMENT;
   if (num_rows == 0) return MXQ_OK;
   if (psum == nullptr || m_indices == nullptr) return MXQ_ERR_INVALID_ARGUMENT;
-  int64_t blocks = ceil_div(num_rows, 1024 * 4);
-  if (blocks > 256) blocks = 256;
-  m_indices_from_psum_kernel<<<(unsigned)blocks, 1024,
+  int64_t blocks = ceil_div(num_rows, kPsumThreads);
+  if (blocks > kPsumBlocks) blocks = kPsumBlocks;
+  m_indices_from_psum_kernel<<<(unsigned)blocks, kPsumThreads,
                                (size_t)2 * E * sizeof(int64_t),
                                as_stream(stream)>>>(psum, E, align, num_rows,
                                                     m_indices);

@@ -19,7 +19,10 @@ def i32(a):
 
 @pytest.mark.parametrize("counts,align", [([3, 0, 130, 1], 128),
                                           ([127, 129, 1, 255, 0, 2], 128),
-                                          ([0, 0, 0], 16), ([5] * 40, 8)])
+                                          ([0, 0, 0], 16), ([5] * 40, 8),
+                                          # 1024 experts, 1.1 M rows: several
+                                          # passes of the whole grid
+                                          (list(range(0, 2048, 2)), 128)])
 def test_m_indices_from_psum(ora, counts, align):
     _, psum, _, total = build_layout(counts, align, 1)
     say("m_indices_from_psum counts=%s align=%d" % (counts[:6], align))
