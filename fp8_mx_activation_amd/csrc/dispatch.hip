@@ -20,7 +20,9 @@
 // threads: 512 up to 512 local experts, else 1024.  At 68 VGPRs a 1024-thread
 // block is the only one on its CU, while three 512-thread blocks fit; on
 // MI355X the 512-thread block took 5.3 us instead of 5.6 us for T=128 top-8
-// over 32 experts, and 6.1 us instead of 9.4 us for T=512 top-8.
+// over 32 experts, and 6.1 us instead of 9.4 us for T=512 top-8.  Each
+// thread loads PER ids of the routing, the power of two that covers it
+// (loads past the routing would only repeat its last id).
 #include "layout_device.hpp"
 #include "mxq_host.hpp"
 
@@ -36,7 +38,7 @@ __host__ __device__ inline int fused_lds_ints(int E) {
   return (3 * E + 1 + 3) & ~3;
 }
 
-template <int G, int NT>
+template <int G, int NT, int PER>
 __global__ __launch_bounds__(NT) void layout_scatter_quant_kernel(
     const int32_t* __restrict__ ids, int32_t K, int32_t A, int32_t begin,
     int32_t E, int32_t kind, int32_t block_e, int32_t cap, int64_t num_rows,
@@ -46,7 +48,7 @@ __global__ __launch_bounds__(NT) void layout_scatter_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ld_x, int32_t H,
     uint8_t* __restrict__ q, int64_t ld_q, uint8_t* __restrict__ s,
     int64_t ld_s) {
-  constexpr int kIdsPerThread = kFusedMaxAssignments / NT;
+  constexpr int kIdsPerThread = PER;
   extern __shared__ __align__(16) int32_t sm[];
   __shared__ int32_t wsum[16];
   __shared__ int32_t tok_e[MXQ_MAX_TOPK];  // local expert of (t, j), or -1
@@ -220,12 +222,27 @@ extern "C" mxq_status moe_layout_scatter_quant(
         num_rows, counts, expert_offsets, m_indices, masked_m, src2dst,
         overflow_flag, x, ld_x, H, q, ld_q, scales, ld_s);
   };
-  if (E <= 512) {
-    if (G == 128) launch(layout_scatter_quant_kernel<128, 512>, 512);
-    else launch(layout_scatter_quant_kernel<32, 512>, 512);
+  const int nt = E <= 512 ? 512 : 1024;
+  int per = 1;
+  while ((int64_t)nt * per < A) per *= 2;  // A <= kFusedMaxAssignments
+  if (nt == 512) {
+    if (G == 128) {
+      if (per <= 2) launch(layout_scatter_quant_kernel<128, 512, 2>, 512);
+      else if (per == 4) launch(layout_scatter_quant_kernel<128, 512, 4>, 512);
+      else launch(layout_scatter_quant_kernel<128, 512, 8>, 512);
+    } else {
+      if (per <= 2) launch(layout_scatter_quant_kernel<32, 512, 2>, 512);
+      else if (per == 4) launch(layout_scatter_quant_kernel<32, 512, 4>, 512);
+      else launch(layout_scatter_quant_kernel<32, 512, 8>, 512);
+    }
   } else {
-    if (G == 128) launch(layout_scatter_quant_kernel<128, 1024>, 1024);
-    else launch(layout_scatter_quant_kernel<32, 1024>, 1024);
+    if (G == 128) {
+      if (per <= 2) launch(layout_scatter_quant_kernel<128, 1024, 2>, 1024);
+      else launch(layout_scatter_quant_kernel<128, 1024, 4>, 1024);
+    } else {
+      if (per <= 2) launch(layout_scatter_quant_kernel<32, 1024, 2>, 1024);
+      else launch(layout_scatter_quant_kernel<32, 1024, 4>, 1024);
+    }
   }
   return launch_status();
 }

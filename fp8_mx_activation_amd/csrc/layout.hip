@@ -372,8 +372,14 @@ __global__ __launch_bounds__(1024) void layout_assign_kernel(
 // over 32 masked experts 4.1 against 6.2 us, over 256 compact experts 4.8
 // against 7.4 us; 512 x 8 4.6-4.9 against 8.3-9.2 us; 1024 x 4 5.4 against
 // 10.1 us; 2048 x 2 7.5 against 10.1 us; but 4096 x 1 12.4 against 8.9 us,
-// where 4096 blocks each count the whole routing.
-template <int NT>
+// where 4096 blocks each count the whole routing.  Each thread loads PER ids,
+// the power of two that covers the routing with NT threads (loads past the
+// routing would only repeat its last id): with 512 threads up to 512 tokens
+// (the block scan needs at least E threads, 512 up to 512 experts) and 256
+// above, 128 x 8 over 32 masked experts took 3.6 against 4.15 us with 256
+// threads of 16 loads, over 256 compact experts 4.2 against 4.85 us, 512 x 8
+// 4.3 against 4.8 us; at 2048 x 2, 512 threads took 8.9 against 7.6 us.
+template <int NT, int PER>
 __global__ __launch_bounds__(NT) void layout_token_kernel(
     const int32_t* __restrict__ ids, int32_t K, int32_t A, int32_t begin,
     int32_t E, int32_t kind, int32_t block_e, int32_t cap, int64_t num_rows,
@@ -389,7 +395,7 @@ __global__ __launch_bounds__(NT) void layout_token_kernel(
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.x;
   const int a0 = (int)t * K;
-  constexpr int kPer = (int)(kSingleMax / NT);
+  constexpr int kPer = PER;
   // every id and this token's own ids, all in flight together (indices
   // clamped, no branch)
   int idv[kPer];
@@ -498,16 +504,27 @@ mxq_status layout_launch(const int32_t* topk_ids, int64_t T, int32_t K,
   const int32_t cap = kind == MXQ_LAYOUT_MASKED ? capacity : 0;
   if (layout_per_token(A, T, E)) {
     const size_t lds = (size_t)(3 * E + 1) * sizeof(int32_t);
-    if (E <= 256)
-      layout_token_kernel<256><<<(unsigned)T, 256, lds, s>>>(
+    const int nt = E > 512 ? 1024 : (E > 256 || T <= 512 ? 512 : 256);
+    int per = 1;
+    while ((int64_t)nt * per < A) per *= 2;  // A <= kSingleMax
+    auto launch = [&](auto kernel) {
+      kernel<<<(unsigned)T, nt, lds, s>>>(
           topk_ids, K, (int32_t)A, expert_begin, E, (int32_t)kind, block_e,
           cap, num_rows, counts, expert_offsets, m_indices, masked_m, src2dst,
           overflow_flag);
-    else
-      layout_token_kernel<1024><<<(unsigned)T, 1024, lds, s>>>(
-          topk_ids, K, (int32_t)A, expert_begin, E, (int32_t)kind, block_e,
-          cap, num_rows, counts, expert_offsets, m_indices, masked_m, src2dst,
-          overflow_flag);
+    };
+    if (nt == 256) {
+      if (per <= 4) launch(layout_token_kernel<256, 4>);
+      else if (per == 8) launch(layout_token_kernel<256, 8>);
+      else launch(layout_token_kernel<256, 16>);
+    } else if (nt == 512) {
+      if (per <= 2) launch(layout_token_kernel<512, 2>);
+      else if (per == 4) launch(layout_token_kernel<512, 4>);
+      else launch(layout_token_kernel<512, 8>);
+    } else {
+      if (per <= 2) launch(layout_token_kernel<1024, 2>);
+      else launch(layout_token_kernel<1024, 4>);
+    }
     return launch_status();
   }
   const bool single = A <= kSingleMax;
