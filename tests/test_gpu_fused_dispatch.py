@@ -116,6 +116,24 @@ def test_block_size_boundary(ora):
         fused_case(ora, x, ids, 511, E, "masked", 32, cap=2)
 
 
+def test_many_experts_and_many_ids_per_thread(ora):
+    """700 local experts (1024-thread blocks) with 3200 assignments, so each
+    thread loads four ids of the routing; the layout alone takes the same
+    block shape (one block per token) and is compared too."""
+    rng = np.random.default_rng(36)
+    T, K, H = 400, 8, 512
+    x = si.gaussian_bf16(rng, (T, H))
+    ids = si.uniform_topk(rng, T, 800, K)
+    fused_case(ora, x, ids, 50, 700, "compact", 32)
+    fused_case(ora, x, ids, 0, 700, "masked", 128, cap=6)
+    ref = ora.moe_layout(ids, 50, 700, "compact")
+    lay = mxq.moe_layout(i32_to_dev(ids), 50, 700, "compact")
+    torch.cuda.synchronize()
+    for key in ("counts", "expert_offsets", "masked_m", "src2dst",
+                "m_indices"):
+        assert_equal(host(lay[key]), ref[key], "layout " + key)
+
+
 def test_same_as_two_calls_and_limits():
     """Byte-identical to moe_layout + moe_scatter_quant on the GPU; more than
     4096 assignments is refused; T = 0 gives the empty layout."""
