@@ -17,7 +17,8 @@ Workloads (shapes follow the pages' DeepSeek-class models: hidden 7168, a
                   channels scaled x100, block 128, group 128       seed 303
   live_rows       24576 x 7168 padded rows = 8 segments of 3072, live counts
                   [14]*8, group 32 (e8m0)                           seed 404
-  requant_combine T=16384, H=4096: fp8 rows with per-token scales 2^U,
+  requant_combine T=16384, H=4096: fp8 rows (bytes drawn field by field,
+                  one +-448 per row) with per-token scales 2^U,
                   U ~ U[-8, 4]; 128 experts top-8 uniform, block 128  seed 505
   fp8_dispatch    24576 x 7168 e4m3 rows (3072 x 8 padded receive buffer)
                   with group-128 fp32 scales, upscaled over the first
@@ -121,18 +122,19 @@ def softmax_weights(rng: np.random.Generator, T: int, K: int) -> np.ndarray:
 
 def per_token_fp8(rng: np.random.Generator, T: int, H: int,
                   log2_lo: float = -8.0, log2_hi: float = 4.0):
-    """fp8 e4m3fn rows whose largest magnitude is 448, with per-token fp32
-    scales 2^U, U ~ U[log2_lo, log2_hi].  The bytes come from torch's
-    float32 -> float8_e4m3fn cast."""
-    z = rng.standard_normal((T, H), dtype=np.float32)
-    m = np.abs(z).max(axis=1, keepdims=True) if H else np.ones((T, 1))
-    m[m == 0] = 1.0
-    y = (z * (np.float32(448.0) / m.astype(np.float32))).astype(np.float32)
-    y = np.clip(y, -448.0, 448.0)
-    q = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    """fp8 e4m3fn rows whose largest magnitude is 448, as a per-token absmax
+    quantizer leaves them, with per-token fp32 scales 2^U,
+    U ~ U[log2_lo, log2_hi].  The bytes are drawn field by field
+    (random_e4m3_bytes), and one random position per row is set to +-448
+    (byte 0x7E with a random sign); no finite e4m3 byte is larger."""
+    q = random_e4m3_bytes(rng, (T, H))
+    if H > 0 and T > 0:
+        pos = rng.integers(0, H, T)
+        sign = (rng.random(T) < 0.5).astype(np.uint8) << 7
+        q[np.arange(T), pos] = np.uint8(0x7E) | sign
     u = rng.uniform(log2_lo, log2_hi, size=T)
     scales = np.exp2(u).astype(np.float32)
-    return q.copy(), scales
+    return q, scales
 
 
 # --------------------------------------------------------------- workloads
