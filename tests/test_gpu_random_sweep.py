@@ -21,7 +21,7 @@ from gpu_util import (CANARY, DEV, assert_equal, bf16_to_dev, f32_to_dev,
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 128
 FUSED_MAX = 4096
 FMT = {128: "ue8m0_g128", 32: "e8m0_g32"}
 ROW_BYTES_BUDGET = 48 << 20     # destination rows x H, per case
